@@ -1,0 +1,209 @@
+"""Throughput of the sequence-parallel masked rotary attention path on one MI355X.
+
+One step = one layer's SP attention for all 8 virtual ranks of the
+32768-token, 32-head, head_dim-128 video workload (``share_32768``): pack Q,
+K and V to per-rank head shards, rotate Q/K, attend over all 32768 keys for
+every rank's 4 heads, and unpack the output.  Every part is exactly 8x one
+rank's share, so the rate equals one rank's.  Inputs are seeded synthetic
+bf16 N(0,1) tensors already resident in HBM.
+
+Prints one JSON line.  ``value`` is attention TFLOP/s over the whole step
+(4 * Nq * Nk_valid * D * H flop per step).  ``roofline`` covers the dominant
+kernel (ltxa_attn_fwd), timed with HIP events on its own stream inside the
+timed region.  ``cpu_baseline`` is the fp64 numpy oracle on a bounded row
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "masked RoPE-attention TFLOP/s and % bf16 MFMA peak at 32K tokens, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WORKLOAD = "share_32768"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_share_32768_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "video_dit_sequence_amd", "csrc", "attn_fwd.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample (0 skips it)")
+    return ap.parse_args()
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != source_digest(ATTN_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, qpos, kpos, budget_s):
+    """Time the oracle on a bounded sample: blocks of 256 query rows of
+    successive heads against all 32768 keys (rotary on the rows and keys,
+    then attention), until the time budget is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    f64 = lambda t: t.to(torch.float64).numpy()
+    rows_per_block = 256
+    flops = 0.0
+    done_rows = 0
+    heads_used = 0
+    t0 = time.perf_counter()
+    for h in range(w.full_heads):
+        kh = f64(k[:, :, h:h + 1])
+        vh = f64(v[:, :, h:h + 1])
+        kr = oracle.rope_apply(kh, kpos, w.k_max_pos, w.theta)
+        heads_used += 1
+        for r0 in range(0, w.nq, rows_per_block):
+            rows = np.arange(r0, r0 + rows_per_block)
+            qr = oracle.rope_apply(f64(q[:, r0:r0 + rows_per_block, h:h + 1]), qpos[rows],
+                                   w.q_max_pos, w.theta)
+            oracle.attention(qr, kr, vh, w.nk_valid, w.scale)
+            flops += 4.0 * rows_per_block * w.nk_valid * w.head_dim
+            done_rows += rows_per_block
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_rows} query rows over {heads_used} head(s) x {w.nk_valid} keys, "
+                      f"head_dim {w.head_dim}, fp64 numpy (rotary + attention), {dt:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    global torch
+    import torch
+    from video_dit_sequence_amd import ltxa
+    from video_dit_sequence_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[WORKLOAD]
+    P, H, D = w.world_sizes[0], w.full_heads, w.head_dim
+    q_cpu, k_cpu, v_cpu = wl.qkv(w, heads=H)             # [1, 32768, 32, 128] each
+    qpos, kpos = wl.positions(w)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    pos = torch.from_numpy(qpos).to(dev)
+    share = ltxa.SpShare(max_tokens=32768, num_heads=H, head_dim=D, world_size=P)
+    n_pad = share.set_seqlen(w.nq_valid)
+    B, N, Hl = w.B, n_pad, H // P
+
+    # Preallocated per-rank buffers (the AttentionManager's receive buffers).
+    qs = torch.empty((P, B, N, Hl, D), dtype=torch.bfloat16, device=dev)
+    ks, vs, os_ = torch.empty_like(qs), torch.empty_like(qs), torch.empty_like(qs)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record=None):
+        marks = [ev() for _ in range(5)] if record is not None else None
+        if marks: marks[0].record(stream)
+        ltxa.sp_pack(q, P, out=qs)
+        ltxa.sp_pack(k, P, out=ks)
+        ltxa.sp_pack(v, P, out=vs)
+        if marks: marks[1].record(stream)
+        ltxa.rope_qk(qs.view(P * B, N, Hl, D), pos, w.q_max_pos, ks.view(P * B, N, Hl, D), pos,
+                     w.k_max_pos, w.theta)
+        if marks: marks[2].record(stream)
+        ltxa.attn_fwd(qs.view(P * B, N, Hl, D), ks.view(P * B, N, Hl, D), vs.view(P * B, N, Hl, D),
+                      nk_valid=w.nk_valid, out=os_.view(P * B, N, Hl, D))
+        if marks: marks[3].record(stream)
+        ltxa.sp_unpack(os_, out=out)
+        if marks: marks[4].record(stream)
+        if record is not None:
+            record.append(marks)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    records = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(records)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    phases = {"pack_qkv": [], "rope_qk": [], "attn_fwd": [], "unpack_o": []}
+    for m in records:
+        for i, name in enumerate(phases):
+            phases[name].append(m[i].elapsed_time(m[i + 1]))
+    avg = {k_: sum(x) / len(x) for k_, x in phases.items()}
+
+    attn_flop = 4.0 * N * w.nk_valid * D * H            # one launch covers all P ranks' heads
+    step_tflops = attn_flop / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = attn_flop / (avg["attn_fwd"] * 1e-3) / 1e12
+    traffic = traffic_per_launch()
+    pack_bytes = 3 * 2.0 * B * N * H * D * 2
+    unpack_bytes = 2.0 * B * N * H * D * 2
+    rope_bytes = 2 * 2.0 * B * N * H * D * 2 + N * 3 * 4
+
+    line = {
+        "metric": METRIC,
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "tokens": N, "valid_tokens": w.nq_valid, "heads": H,
+                   "head_dim": D, "virtual_ranks": P, "heads_per_rank": Hl, "batch": B,
+                   "grid_txy": list(w.q_grid), "rope_theta": w.theta},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "ltxa_attn_fwd",
+                     "flop_per_launch": attn_flop, "avg_launch_ms": round(avg["attn_fwd"], 4)},
+        "phases_ms": {k_: round(x, 4) for k_, x in avg.items()},
+        "hbm_GBps": {
+            "pack_qkv": round(pack_bytes / (avg["pack_qkv"] * 1e-3) / 1e9, 1),
+            "rope_qk": round(rope_bytes / (avg["rope_qk"] * 1e-3) / 1e9, 1),
+            "unpack_o": round(unpack_bytes / (avg["unpack_o"] * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, qpos, kpos, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

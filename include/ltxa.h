@@ -1,0 +1,153 @@
+/*
+ * ltxa.h -- C ABI of libltxa.so: masked rotary attention for one
+ * sequence-parallel (SP) rank's share, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two source pages:
+ *  - LTX-2 multi-GPU docs, "Sequence Parallelism (SP)": the video sequence is
+ *    padded to a multiple of world_size (padded keys masked, padded rows
+ *    dropped), Q/K/V are exchanged so that each rank holds every token for a
+ *    subset of heads, each rank runs global attention over all tokens for its
+ *    heads, and results are shuffled back; the exchange moves bytes only and
+ *    num_heads must be divisible by world_size ("What it is", "How the
+ *    forward pass works", "API / AttentionManager").
+ *  - FastVideo API, fastvideo.models.encoders.gemma: LTXRopeType (INTERLEAVED
+ *    pairs 2i, 2i+1), precompute_ltx_freqs_cis (positions normalised by a
+ *    per-axis max_pos, base theta) and apply_ltx_rotary_emb.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are caller-owned DEVICE memory, contiguous, row-major.  "BSHD"
+ *    means [batch, tokens, heads, head_dim] with head_dim fastest.
+ *  - bf16 means IEEE bfloat16 stored as 16-bit words.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it: they never synchronise the host, allocate, free, or
+ *    keep a pointer after returning.  Completion follows stream order.
+ *  - Every argument is checked before anything is enqueued; on any error the
+ *    call returns a negative LTXA_E_* code and enqueues nothing.  The
+ *    exception is LTXA_E_HIP, which reports a failed launch.
+ *  - The library holds no mutable global state; calls are thread-safe.
+ *  - Sizes are 64-bit where they count tokens or elements.
+ */
+#ifndef LTXA_H
+#define LTXA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LTXA_VERSION 100 /* major*100 + minor */
+
+enum ltxa_status {
+  LTXA_OK = 0,
+  LTXA_E_NULL = -1,         /* a required pointer is NULL */
+  LTXA_E_SHAPE = -2,        /* a size is out of range (see each call) */
+  LTXA_E_DIVISIBILITY = -3, /* heads or tokens not divisible by world_size */
+  LTXA_E_ALIGN = -4,        /* a device pointer is not 16-byte aligned */
+  LTXA_E_ALIAS = -5,        /* buffers that must be distinct overlap */
+  LTXA_E_HIP = -6,          /* the HIP runtime reported a launch error */
+  LTXA_E_RANGE = -7         /* a size overflows 64-bit byte counts or grid limits */
+};
+
+/* Library version, LTXA_VERSION of the build. */
+int ltxa_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ltxa_status_string(int status);
+
+/*
+ * ltxa_sp_pack -- token-major -> per-rank head shards (the one-GPU share of
+ * the SP all2all; "What it is" on the SP page).
+ *
+ *   src: [batch, n_tokens, heads, head_dim] elements of elem_bytes each.
+ *   dst: [world_size, batch, n_tokens, heads/world_size, head_dim].
+ *   dst[p][b][n][j][:] = src[b][n][p*(heads/world_size) + j][:]
+ *
+ * Rank p's receive buffer is dst[p], itself a BSHD tensor over all tokens
+ * with heads/world_size heads.  A pure byte copy.
+ * Errors: E_NULL (src or dst NULL); E_SHAPE (a size < 1, or elem_bytes not in
+ * {1,2,4,8}); E_DIVISIBILITY (heads % world_size != 0, or n_tokens %
+ * world_size != 0: the SP page pads the sequence to a multiple of
+ * world_size first); E_ALIAS (src and dst byte ranges overlap); E_RANGE.
+ * Any pointer alignment is accepted; 16-byte aligned rows are fastest.
+ */
+int ltxa_sp_pack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
+                 int32_t heads, int32_t head_dim, int32_t world_size,
+                 int32_t elem_bytes, void* stream);
+
+/*
+ * ltxa_sp_unpack -- inverse of ltxa_sp_pack (results shuffled back to token
+ * order; SP page, "What it is").  Same arguments with src and dst roles
+ * swapped: src is [world_size, batch, n_tokens, heads/world_size, head_dim],
+ * dst is [batch, n_tokens, heads, head_dim].  Same errors.
+ */
+int ltxa_sp_unpack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
+                   int32_t heads, int32_t head_dim, int32_t world_size,
+                   int32_t elem_bytes, void* stream);
+
+/*
+ * ltxa_rope_qk -- interleaved rotary embedding applied in place to Q and K
+ * (FastVideo gemma page: LTXRopeType INTERLEAVED, precompute_ltx_freqs_cis,
+ * apply_ltx_rotary_emb).
+ *
+ *   q: bf16 BSHD [batch, nq, heads, head_dim], rotated in place, may be NULL.
+ *   k: bf16 BSHD [batch, nk, heads, head_dim], rotated in place, may be NULL.
+ *   q_pos / k_pos: DEVICE int32 [nq, q_axes] / [nk, k_axes] integer
+ *     positions (axis order t, x, y for 3 axes; time for 1 axis), shared by
+ *     every batch entry and head.
+ *   q_max_pos / k_max_pos: HOST arrays of q_axes / k_axes positive values,
+ *     read during the call only.
+ *   theta: frequency base (the pages' default is 10000).
+ *
+ * With A axes and head_dim/2 channel pairs, axis a owns the n_ax =
+ * floor(head_dim/2/A) consecutive pairs starting at a*n_ax; pair a*n_ax + k
+ * turns by phi = (pos[a] / max_pos[a]) * theta^(-k/n_ax); the
+ * (head_dim/2) mod A highest pairs are left as they are.  Pair (x0, x1) =
+ * channels (2i, 2i+1) becomes (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos
+ * phi).  Angles and products are computed in fp32 from fp64 per-pair
+ * frequencies; results are rounded to bf16 (nearest even).
+ * Errors: E_NULL (both q and k NULL, or a non-NULL tensor without its
+ * positions or max_pos); E_SHAPE (batch, heads or a token count < 1, head_dim
+ * odd or not in [2, 256], axes not in {1,2,3} or more axes than pairs,
+ * max_pos <= 0 or not finite, theta <= 0 or not finite); E_ALIGN (q, k or a
+ * position array not 16-byte aligned, or head_dim*2 not a multiple of 16);
+ * E_ALIAS (q and k overlap); E_RANGE.
+ */
+int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
+                 const double* q_max_pos,
+                 void* k, const int32_t* k_pos, int64_t nk, int32_t k_axes,
+                 const double* k_max_pos,
+                 int64_t batch, int32_t heads, int32_t head_dim, double theta,
+                 void* stream);
+
+/*
+ * ltxa_attn_fwd -- key-padding-masked scaled-dot-product attention over all
+ * tokens for the given heads (SP page, "What it is": attention stays global;
+ * "How the forward pass works" step 1: padded keys are masked out).
+ *
+ *   q: bf16 BSHD [batch, nq, heads, head_dim]
+ *   k, v: bf16 BSHD [batch, nk_pad, heads, head_dim]
+ *   o: bf16 BSHD [batch, nq, heads, head_dim] (written)
+ *   lse: fp32 [batch, heads, nq] natural-log log-sum-exp of the scaled
+ *     scores per query row, or NULL.
+ *   For each b, h and query i: s_ij = scale * <q_i, k_j> over keys
+ *   j < nk_valid only; o_i = sum_j softmax_j(s_i) v_j.  Keys at or past
+ *   nk_valid are never read, so their contents (NaN included) cannot reach
+ *   the output.  Query rows past the caller's valid length are computed like
+ *   any other row.
+ * Arithmetic: bf16 products with fp32 accumulation, fp32 online softmax,
+ * fp32 -> bf16 output rounding (nearest even).
+ * Errors: E_NULL (q, k, v or o NULL); E_SHAPE (batch, heads, nq < 1;
+ * head_dim not 64 or 128; nk_valid not in [1, nk_pad]; scale not finite and
+ * > 0); E_ALIGN (a pointer not 16-byte aligned); E_ALIAS (o or lse overlaps
+ * q, k, v, or each other); E_RANGE.
+ */
+int ltxa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                  int64_t nk_pad, int64_t nk_valid, float scale, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* LTXA_H */

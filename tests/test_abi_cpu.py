@@ -1,0 +1,150 @@
+"""CPU checks of the C ABI: the library loads, exports exactly what
+include/ltxa.h declares, and rejects bad arguments with the documented codes
+before touching the GPU.  Also the host-side SpShare bookkeeping (LTX-2 SP
+page, "API / AttentionManager" and "Usage")."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from video_dit_sequence_amd import ltxa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ltxa.h")
+
+# Fake, 256-byte aligned device addresses: validation never dereferences them
+# and no call below passes validation, so nothing is launched.
+A, B, C, D_, E = (0x10000000 * i for i in range(1, 6))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ltxa.LIB_PATH):
+        from video_dit_sequence_amd import build
+        build.build()
+    return ltxa.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(ltxa_\w+)\s*\(", text, re.M)))
+
+
+def header_constant(name):
+    text = open(HEADER).read()
+    m = re.search(rf"{name}\s*=?\s*(-?\d+)", text)
+    return int(m.group(1))
+
+
+def test_exports_match_header(L):
+    declared = header_functions()
+    assert declared == sorted(ltxa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ltxa.LIB_PATH], capture_output=True, text=True)
+    exported = sorted(l.split()[-1] for l in out.stdout.splitlines() if " T ltxa_" in l)
+    assert exported == declared
+
+
+def test_version_and_status_strings(L):
+    assert ltxa.version() == header_constant("LTXA_VERSION")
+    for code in (ltxa.LTXA_OK, ltxa.LTXA_E_NULL, ltxa.LTXA_E_SHAPE, ltxa.LTXA_E_DIVISIBILITY,
+                 ltxa.LTXA_E_ALIGN, ltxa.LTXA_E_ALIAS, ltxa.LTXA_E_HIP, ltxa.LTXA_E_RANGE):
+        s = ltxa.status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in ltxa.status_string(12345)
+    for name, val in (("LTXA_E_NULL", -1), ("LTXA_E_SHAPE", -2), ("LTXA_E_DIVISIBILITY", -3),
+                      ("LTXA_E_ALIGN", -4), ("LTXA_E_ALIAS", -5), ("LTXA_E_HIP", -6),
+                      ("LTXA_E_RANGE", -7)):
+        assert header_constant(name) == val == getattr(ltxa, name)
+
+
+@pytest.mark.parametrize("fn", ["ltxa_sp_pack", "ltxa_sp_unpack"])
+def test_perm_errors(L, fn):
+    f = getattr(L, fn)
+    assert f(None, B, 1, 8, 4, 64, 2, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, None, 1, 8, 4, 64, 2, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, 0, 8, 4, 64, 2, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, 1, 8, 4, 0, 2, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, 1, 8, 4, 64, 0, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, 1, 8, 4, 64, 2, 3, None) == ltxa.LTXA_E_SHAPE
+    # heads % world_size (the AttentionManager rule) and tokens % world_size
+    # (the sequence is padded to a multiple of world_size first).
+    assert f(A, B, 1, 232, 2, 64, 4, 2, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, 1, 231, 4, 64, 4, 2, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, A + 64, 1, 8, 4, 64, 2, 2, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, 1 << 40, 1 << 20, 64, 128, 8, 2, None) == ltxa.LTXA_E_RANGE
+
+
+def _mp(*vals):
+    return (ctypes.c_double * len(vals))(*vals)
+
+
+def test_rope_errors(L):
+    f = L.ltxa_rope_qk
+    mp3 = _mp(3, 7, 11)
+    ok_q = (A, C, 232, 3, mp3)
+    none = (None, None, 0, 0, None)
+    assert f(*none, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, None, 232, 3, mp3, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, C, 232, 3, None, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(*ok_q, *none, 0, 2, 64, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(*ok_q, *none, 1, 2, 63, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(*ok_q, *none, 1, 2, 512, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, C, 232, 4, _mp(1, 1, 1, 1), *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, C, 232, 3, _mp(3, 0, 11), *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, C, 232, 3, _mp(3, float("nan"), 11), *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(*ok_q, *none, 1, 2, 64, 0.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(*ok_q, *none, 1, 2, 64, float("inf"), None) == ltxa.LTXA_E_SHAPE
+    assert f(A, C, 0, 3, mp3, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(*ok_q, *none, 1, 2, 4, 1e4, None) == ltxa.LTXA_E_ALIGN       # 8-byte rows
+    assert f(A + 2, C, 232, 3, mp3, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, C + 4, 232, 3, mp3, *none, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_ALIGN
+    assert f(*ok_q, A + 256, C, 232, 3, mp3, 1, 2, 64, 1e4, None) == ltxa.LTXA_E_ALIAS
+
+
+def test_attn_errors(L):
+    f = L.ltxa_attn_fwd
+    good = (1, 2, 128, 232, 232, 231, 0.088)
+    assert f(None, B, C, D_, None, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, None, None, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, D_, None, 1, 2, 96, 232, 232, 231, 0.1, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 2, 128, 232, 232, 0, 0.1, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 2, 128, 232, 232, 233, 0.1, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 2, 128, 0, 232, 231, 0.1, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 0, 2, 128, 232, 232, 231, 0.1, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 2, 128, 232, 232, 231, 0.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 2, 128, 232, 232, 231, float("nan"), None) == ltxa.LTXA_E_SHAPE
+    assert f(A + 8, B, C, D_, None, *good, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, D_, E + 4, *good, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, A + 64, None, *good, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, D_, C + 128, *good, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, D_, None, 1 << 30, 1 << 10, 128, 1 << 20, 1 << 20, 1, 0.1, None) == ltxa.LTXA_E_RANGE
+
+
+def test_sp_share_bookkeeping():
+    s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
+    assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096
+    assert s.set_seqlen(32761) == 32768 and s.tokens_per_rank == 4096
+    assert s.set_seqlen(6144) == 6144
+    assert s.set_seqlen(32768) == 32768
+    with pytest.raises(ValueError, match="smaller resolution or fewer frames"):
+        s.set_seqlen(32769)
+    with pytest.raises(ValueError):
+        s.set_seqlen(0)
+    with pytest.raises(ValueError, match="divisible"):
+        ltxa.SpShare(max_tokens=232, num_heads=2, head_dim=64, world_size=4)
+    t = ltxa.SpShare(max_tokens=231, num_heads=4, head_dim=64, world_size=4)
+    assert t.tokens_per_rank_max == 58 and t.set_seqlen(231) == 232
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 8, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ltxa.sp_pack(x, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        ltxa.attn_fwd(x, x, x)

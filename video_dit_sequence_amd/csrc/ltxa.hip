@@ -1,0 +1,104 @@
+// C ABI of libltxa.so (declared in include/ltxa.h): argument checks, then a
+// launch on the caller's stream.  No allocation, no host synchronisation, no
+// global mutable state.
+#include <cmath>
+
+#include "kernels.h"
+#include "ltxa.h"
+#include "validate.h"
+
+#define LTXA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LTXA_OK : LTXA_E_HIP; }
+
+// Frequencies of the interleaved rotary schedule, in fp64 on the host: with
+// A axes and head_dim/2 pairs, axis a owns pairs [a*n_ax, (a+1)*n_ax), and
+// pair a*n_ax + j turns by pos[a] * theta^(-j/n_ax) / max_pos[a]; the
+// leftover highest pairs stay unrotated.
+ltxa::RopeTable rope_table(int32_t head_dim, int32_t axes, const double* max_pos, double theta) {
+  ltxa::RopeTable t;
+  const int pairs = head_dim / 2;
+  const int per_axis = pairs / axes;
+  for (int i = 0; i < 128; ++i) {
+    t.coef[i] = 0.0f;
+    t.axis[i] = -1;
+  }
+  for (int a = 0; a < axes; ++a)
+    for (int j = 0; j < per_axis; ++j) {
+      const int i = a * per_axis + j;
+      t.coef[i] = static_cast<float>(std::pow(theta, -static_cast<double>(j) / per_axis) / max_pos[a]);
+      t.axis[i] = a;
+    }
+  return t;
+}
+
+}  // namespace
+
+LTXA_EXPORT int ltxa_version(void) { return LTXA_VERSION; }
+
+LTXA_EXPORT const char* ltxa_status_string(int status) {
+  switch (status) {
+    case LTXA_OK: return "ok";
+    case LTXA_E_NULL: return "a required pointer is NULL";
+    case LTXA_E_SHAPE: return "a size is out of range";
+    case LTXA_E_DIVISIBILITY: return "heads or tokens are not divisible by world_size";
+    case LTXA_E_ALIGN: return "a device pointer or row is not 16-byte aligned";
+    case LTXA_E_ALIAS: return "buffers that must be distinct overlap";
+    case LTXA_E_HIP: return "the HIP runtime reported a launch error";
+    case LTXA_E_RANGE: return "a size overflows byte counts or grid limits";
+    default: return "unknown ltxa status";
+  }
+}
+
+LTXA_EXPORT int ltxa_sp_pack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
+                             int32_t heads, int32_t head_dim, int32_t world_size,
+                             int32_t elem_bytes, void* stream) {
+  ltxa::PermPlan plan;
+  const int rc = ltxa::check_perm(src, dst, batch, n_tokens, heads, head_dim, world_size,
+                                  elem_bytes, &plan);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_perm(src, dst, plan, world_size, true,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_sp_unpack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
+                               int32_t heads, int32_t head_dim, int32_t world_size,
+                               int32_t elem_bytes, void* stream) {
+  ltxa::PermPlan plan;
+  const int rc = ltxa::check_perm(src, dst, batch, n_tokens, heads, head_dim, world_size,
+                                  elem_bytes, &plan);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_perm(src, dst, plan, world_size, false,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
+                             const double* q_max_pos, void* k, const int32_t* k_pos, int64_t nk,
+                             int32_t k_axes, const double* k_max_pos, int64_t batch, int32_t heads,
+                             int32_t head_dim, double theta, void* stream) {
+  const int rc = ltxa::check_rope(q, q_pos, nq, q_axes, q_max_pos, k, k_pos, nk, k_axes, k_max_pos,
+                                  batch, heads, head_dim, theta);
+  if (rc) return rc;
+  auto s = static_cast<hipStream_t>(stream);
+  if (q) {
+    const int r = launch_status(ltxa::launch_rope(static_cast<uint16_t*>(q), q_pos, nq, q_axes, batch,
+                                                  heads, head_dim,
+                                                  rope_table(head_dim, q_axes, q_max_pos, theta), s));
+    if (r) return r;
+  }
+  if (k)
+    return launch_status(ltxa::launch_rope(static_cast<uint16_t*>(k), k_pos, nk, k_axes, batch, heads,
+                                           head_dim, rope_table(head_dim, k_axes, k_max_pos, theta), s));
+  return LTXA_OK;
+}
+
+LTXA_EXPORT int ltxa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                              int64_t nk_pad, int64_t nk_valid, float scale, void* stream) {
+  const int rc = ltxa::check_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid, scale);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid,
+                                         scale, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,132 @@
+// Host-only argument checks for the ltxa C ABI.  Pure integer arithmetic: no
+// HIP calls, so every error path can be exercised without a GPU.
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+
+#include "ltxa.h"
+
+namespace ltxa {
+
+constexpr int64_t kMaxBytes = INT64_C(1) << 52;  // keeps every byte offset far from overflow
+
+// a * b, or -1 if it would exceed kMaxBytes.
+inline int64_t mul_capped(int64_t a, int64_t b) {
+  if (a < 0 || b < 0) return -1;
+  if (a == 0 || b == 0) return 0;
+  if (a > kMaxBytes / b) return -1;
+  return a * b;
+}
+
+inline int64_t mul4_capped(int64_t a, int64_t b, int64_t c, int64_t d) {
+  int64_t ab = mul_capped(a, b);
+  if (ab < 0) return -1;
+  int64_t abc = mul_capped(ab, c);
+  if (abc < 0) return -1;
+  return mul_capped(abc, d);
+}
+
+inline bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  auto pa = reinterpret_cast<uintptr_t>(a);
+  auto pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + static_cast<uintptr_t>(b_bytes) && pb < pa + static_cast<uintptr_t>(a_bytes);
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct PermPlan {
+  int64_t bytes;  // bytes of each tensor
+  int64_t rows;   // batch * n_tokens
+  int64_t chunk;  // bytes of one (token, rank) head block: heads/P * head_dim * elem
+};
+
+inline int check_perm(const void* src, const void* dst, int64_t batch, int64_t n_tokens,
+                      int32_t heads, int32_t head_dim, int32_t world_size,
+                      int32_t elem_bytes, PermPlan* plan) {
+  if (!src || !dst) return LTXA_E_NULL;
+  if (batch < 1 || n_tokens < 1 || heads < 1 || head_dim < 1 || world_size < 1)
+    return LTXA_E_SHAPE;
+  if (!(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4 || elem_bytes == 8))
+    return LTXA_E_SHAPE;
+  if (heads % world_size != 0 || n_tokens % world_size != 0) return LTXA_E_DIVISIBILITY;
+  int64_t bytes = mul4_capped(batch, n_tokens, heads, mul_capped(head_dim, elem_bytes));
+  if (bytes < 0) return LTXA_E_RANGE;
+  int64_t chunk = static_cast<int64_t>(heads / world_size) * head_dim * elem_bytes;
+  // Grid: y = world_size (<= 65535); x counts 16-byte vectors per rank slab.
+  if (world_size > 65535) return LTXA_E_RANGE;
+  if (bytes / world_size > (INT64_C(1) << 40)) return LTXA_E_RANGE;
+  if (overlap(src, bytes, dst, bytes)) return LTXA_E_ALIAS;
+  plan->bytes = bytes;
+  plan->rows = batch * n_tokens;
+  plan->chunk = chunk;
+  return LTXA_OK;
+}
+
+inline int check_rope_tensor(const void* x, const int32_t* pos, int64_t n, int32_t axes,
+                             const double* max_pos, int32_t head_dim) {
+  if (!pos || !max_pos) return LTXA_E_NULL;
+  if (n < 1) return LTXA_E_SHAPE;
+  if (axes < 1 || axes > 3 || axes > head_dim / 2) return LTXA_E_SHAPE;
+  for (int a = 0; a < axes; ++a)
+    if (!(std::isfinite(max_pos[a]) && max_pos[a] > 0.0)) return LTXA_E_SHAPE;
+  if (!aligned16(x) || !aligned16(pos)) return LTXA_E_ALIGN;
+  return LTXA_OK;
+}
+
+inline int check_rope(const void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
+                      const double* q_max_pos, const void* k, const int32_t* k_pos, int64_t nk,
+                      int32_t k_axes, const double* k_max_pos, int64_t batch, int32_t heads,
+                      int32_t head_dim, double theta) {
+  if (!q && !k) return LTXA_E_NULL;
+  if (batch < 1 || heads < 1) return LTXA_E_SHAPE;
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2 != 0) return LTXA_E_SHAPE;
+  if (!(std::isfinite(theta) && theta > 0.0)) return LTXA_E_SHAPE;
+  if ((head_dim * 2) % 16 != 0) return LTXA_E_ALIGN;
+  int64_t qb = 0, kb = 0;
+  if (q) {
+    int rc = check_rope_tensor(q, q_pos, nq, q_axes, q_max_pos, head_dim);
+    if (rc) return rc;
+    qb = mul4_capped(batch, nq, heads, int64_t(head_dim) * 2);
+    if (qb < 0 || mul_capped(nq, q_axes) < 0) return LTXA_E_RANGE;
+  }
+  if (k) {
+    int rc = check_rope_tensor(k, k_pos, nk, k_axes, k_max_pos, head_dim);
+    if (rc) return rc;
+    kb = mul4_capped(batch, nk, heads, int64_t(head_dim) * 2);
+    if (kb < 0 || mul_capped(nk, k_axes) < 0) return LTXA_E_RANGE;
+  }
+  if (q && k && overlap(q, qb, k, kb)) return LTXA_E_ALIAS;
+  // Grid: one thread per (token, 4 pairs); x dimension holds it.
+  if (nq > (INT64_C(1) << 40) || nk > (INT64_C(1) << 40)) return LTXA_E_RANGE;
+  return LTXA_OK;
+}
+
+inline int check_attn(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, int64_t batch, int32_t heads, int32_t head_dim,
+                      int64_t nq, int64_t nk_pad, int64_t nk_valid, float scale) {
+  if (!q || !k || !v || !o) return LTXA_E_NULL;
+  if (batch < 1 || heads < 1 || nq < 1 || nk_pad < 1) return LTXA_E_SHAPE;
+  if (!(head_dim == 64 || head_dim == 128)) return LTXA_E_SHAPE;
+  if (nk_valid < 1 || nk_valid > nk_pad) return LTXA_E_SHAPE;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return LTXA_E_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return LTXA_E_ALIGN;
+  int64_t qb = mul4_capped(batch, nq, heads, int64_t(head_dim) * 2);
+  int64_t kb = mul4_capped(batch, nk_pad, heads, int64_t(head_dim) * 2);
+  int64_t lb = mul4_capped(batch, heads, nq, 4);
+  if (qb < 0 || kb < 0 || lb < 0) return LTXA_E_RANGE;
+  // Grid x = ceil(nq / rows per block) * batch * heads must stay below 2^31.
+  int64_t qblocks = (nq + 63) / 64;
+  if (mul_capped(qblocks, mul_capped(batch, heads)) < 0 ||
+      qblocks * batch * heads >= (INT64_C(1) << 31))
+    return LTXA_E_RANGE;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb)) return LTXA_E_ALIAS;
+  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+              overlap(lse, lb, o, qb)))
+    return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
+}  // namespace ltxa

@@ -1,0 +1,264 @@
+"""Thin ctypes binding over ``libltxa.so`` (C ABI in ``include/ltxa.h``).
+
+Argument marshalling only: each function checks that it got torch tensors of
+the right dtype on a GPU, passes their device pointers, sizes and the current
+HIP stream to the C entry point of the same name, and raises
+:class:`LtxaError` on a non-zero status.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback.  If the library is
+missing, :func:`lib` raises.
+
+``SpShare`` is the host-side bookkeeping of one sequence-parallel attention
+group (LTX-2 "Sequence Parallelism (SP)" page, "API / AttentionManager":
+``max_tokens`` bound, ``num_heads`` divisible by ``world_size``, per-rank
+buffers of ``ceil(max_tokens / world_size)`` tokens; "How the forward pass
+works" step 1: pad to a multiple of ``world_size``; "Usage": exceeding
+``max_tokens`` raises and asks for a smaller resolution or fewer frames).
+"""
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libltxa.so")
+
+LTXA_OK = 0
+LTXA_E_NULL = -1
+LTXA_E_SHAPE = -2
+LTXA_E_DIVISIBILITY = -3
+LTXA_E_ALIGN = -4
+LTXA_E_ALIAS = -5
+LTXA_E_HIP = -6
+LTXA_E_RANGE = -7
+
+EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
+           "ltxa_rope_qk", "ltxa_attn_fwd")
+
+
+class LtxaError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed with status {status}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if ``libltxa.so`` has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m video_dit_sequence_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        L.ltxa_version.restype = ctypes.c_int
+        L.ltxa_version.argtypes = []
+        L.ltxa_status_string.restype = ctypes.c_char_p
+        L.ltxa_status_string.argtypes = [ctypes.c_int]
+        perm_args = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
+        for name in ("ltxa_sp_pack", "ltxa_sp_unpack"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = perm_args
+        L.ltxa_rope_qk.restype = ctypes.c_int
+        dp = ctypes.POINTER(ctypes.c_double)
+        L.ltxa_rope_qk.argtypes = [vp, vp, i64, i32, dp, vp, vp, i64, i32, dp,
+                                   i64, i32, i32, ctypes.c_double, vp]
+        L.ltxa_attn_fwd.restype = ctypes.c_int
+        L.ltxa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
+                                    ctypes.c_float, vp]
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().ltxa_version()
+
+
+def status_string(status: int) -> str:
+    return lib().ltxa_status_string(status).decode()
+
+
+def _check(call: str, status: int):
+    if status != LTXA_OK:
+        raise LtxaError(call, status)
+
+
+def _stream_ptr(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _gpu(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def sp_pack(src: torch.Tensor, world_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``[B, N, H, D]`` -> ``[P, B, N, H/P, D]`` (``ltxa_sp_pack``)."""
+    _gpu(src, "src")
+    B, N, H, D = src.shape
+    P = int(world_size)
+    if out is None:
+        if P < 1 or H % P:
+            _check("ltxa_sp_pack", LTXA_E_DIVISIBILITY if P >= 1 else LTXA_E_SHAPE)
+        out = torch.empty((P, B, N, H // P, D), dtype=src.dtype, device=src.device)
+    _gpu(out, "out", src.dtype)
+    if out.numel() != src.numel():
+        raise ValueError("out has the wrong number of elements")
+    _check("ltxa_sp_pack", lib().ltxa_sp_pack(src.data_ptr(), out.data_ptr(), B, N, H, D, P,
+                                              src.element_size(), _stream_ptr(src)))
+    return out
+
+
+def sp_unpack(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``[P, B, N, H/P, D]`` -> ``[B, N, H, D]`` (``ltxa_sp_unpack``)."""
+    _gpu(src, "src")
+    P, B, N, Hl, D = src.shape
+    if out is None:
+        out = torch.empty((B, N, P * Hl, D), dtype=src.dtype, device=src.device)
+    _gpu(out, "out", src.dtype)
+    if out.numel() != src.numel():
+        raise ValueError("out has the wrong number of elements")
+    _check("ltxa_sp_unpack", lib().ltxa_sp_unpack(src.data_ptr(), out.data_ptr(), B, N, P * Hl, D, P,
+                                                  src.element_size(), _stream_ptr(src)))
+    return out
+
+
+def _max_pos_array(max_pos: Sequence[float]):
+    return (ctypes.c_double * len(max_pos))(*[float(x) for x in max_pos])
+
+
+def rope_qk(q: Optional[torch.Tensor], q_pos: Optional[torch.Tensor], q_max_pos,
+            k: Optional[torch.Tensor], k_pos: Optional[torch.Tensor], k_max_pos,
+            theta: float = 10000.0) -> None:
+    """Rotate bf16 ``q`` and/or ``k`` (``[B, N, H, D]``) in place (``ltxa_rope_qk``).
+
+    ``q_pos``/``k_pos`` are int32 ``[N, A]`` GPU tensors; ``*_max_pos`` hold
+    ``A`` positive numbers.  Either ``q`` or ``k`` may be ``None``.
+    """
+    ref = q if q is not None else k
+    if ref is None:
+        _check("ltxa_rope_qk", LTXA_E_NULL)
+    B, _, H, D = ref.shape
+    args = []
+    for x, pos, mp, name in ((q, q_pos, q_max_pos, "q"), (k, k_pos, k_max_pos, "k")):
+        if x is None:
+            args += [None, None, 0, 0, None]
+            continue
+        _gpu(x, name, torch.bfloat16)
+        _gpu(pos, f"{name}_pos", torch.int32)
+        if x.dim() != 4 or x.shape[0] != B or x.shape[2] != H or x.shape[3] != D:
+            raise ValueError("q and k must be [B, N, H, D] with the same B, H and D")
+        if pos.dim() != 2 or pos.shape[0] != x.shape[1] or pos.shape[1] != len(mp):
+            raise ValueError(f"{name}_pos must be [N, A] with one max_pos per axis")
+        args += [x.data_ptr(), pos.data_ptr(), x.shape[1], pos.shape[1], _max_pos_array(mp)]
+    _check("ltxa_rope_qk", lib().ltxa_rope_qk(*args, B, H, D, float(theta), _stream_ptr(ref)))
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Optional[int] = None,
+             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Masked attention (``ltxa_attn_fwd``) over bf16 BSHD tensors.
+
+    Keys ``>= nk_valid`` (default: all) are excluded.  ``scale`` defaults to
+    ``1/sqrt(D)``.  ``lse``, if given, is a float32 ``[B, H, Nq]`` tensor.
+    """
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _gpu(t, name, torch.bfloat16)
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Nk, H, D] matching q")
+    nk_valid = Nk if nk_valid is None else int(nk_valid)
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _gpu(out, "out", torch.bfloat16)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+        if lse.shape != (B, H, Nq):
+            raise ValueError("lse must be [B, H, Nq]")
+        lse_ptr = lse.data_ptr()
+    _check("ltxa_attn_fwd", lib().ltxa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                out.data_ptr(), lse_ptr, B, H, D, Nq, Nk, nk_valid,
+                                                scale, _stream_ptr(q)))
+    return out
+
+
+class SpShare:
+    """Bookkeeping of one SP attention group held as ``world_size`` virtual
+    ranks on one GPU (an ``AttentionManager`` analogue)."""
+
+    def __init__(self, max_tokens: int, num_heads: int, head_dim: int, world_size: int):
+        if max_tokens < 1 or num_heads < 1 or head_dim < 1 or world_size < 1:
+            raise ValueError("max_tokens, num_heads, head_dim and world_size must be positive")
+        if num_heads % world_size:
+            raise ValueError(f"num_heads ({num_heads}) must be divisible by world_size ({world_size})")
+        self.max_tokens = int(max_tokens)
+        self.num_heads = int(num_heads)
+        self.head_dim = int(head_dim)
+        self.world_size = int(world_size)
+        self.heads_per_rank = self.num_heads // self.world_size
+        self.tokens_per_rank_max = -(-self.max_tokens // self.world_size)
+        self.n_valid = 0
+        self.n_pad = 0
+
+    def set_seqlen(self, n_valid: int) -> int:
+        """Record this step's token count; returns the padded length."""
+        if n_valid < 1:
+            raise ValueError("the sequence must hold at least one token")
+        if n_valid > self.max_tokens:
+            raise ValueError(f"{n_valid} video tokens exceed max_tokens={self.max_tokens}: "
+                             "use a smaller resolution or fewer frames")
+        self.n_valid = int(n_valid)
+        self.n_pad = -(-self.n_valid // self.world_size) * self.world_size
+        return self.n_pad
+
+    @property
+    def tokens_per_rank(self) -> int:
+        return self.n_pad // self.world_size
+
+
+def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpShare",
+                 q_pos: torch.Tensor, q_max_pos, k_pos: Optional[torch.Tensor] = None,
+                 k_max_pos=None, nk_valid: Optional[int] = None, theta: float = 10000.0,
+                 scale: Optional[float] = None) -> torch.Tensor:
+    """One layer's SP attention for every virtual rank of ``share`` on one GPU.
+
+    ``q``: token-major bf16 ``[B, N_pad, H, D]`` padded to ``share.n_pad``
+    tokens; ``k``/``v``: ``[B, Nk_pad, H, D]`` (the same tensors' token count
+    for self-attention).  Steps (SP page, "How the forward pass works"):
+    exchange heads (``ltxa_sp_pack``), rotate Q/K (``ltxa_rope_qk``), attend
+    over every valid key (``ltxa_attn_fwd``), shuffle back
+    (``ltxa_sp_unpack``) and drop padded rows (a view).  Returns
+    ``[B, share.n_valid, H, D]``.
+    """
+    P = share.world_size
+    B, N, H, D = q.shape
+    Nk = k.shape[1]
+    if N != share.n_pad or H != share.num_heads or D != share.head_dim:
+        raise ValueError("q must be [B, share.n_pad, num_heads, head_dim]")
+    k_pos = q_pos if k_pos is None else k_pos
+    k_max_pos = q_max_pos if k_max_pos is None else k_max_pos
+    nk_valid = share.n_valid if nk_valid is None else nk_valid
+    Hl = H // P
+    qs = sp_pack(q, P).view(P * B, N, Hl, D)
+    ks = sp_pack(k, P).view(P * B, Nk, Hl, D)
+    vs = sp_pack(v, P).view(P * B, Nk, Hl, D)
+    rope_qk(qs, q_pos, q_max_pos, ks, k_pos, k_max_pos, theta)
+    os_ = attn_fwd(qs, ks, vs, nk_valid=nk_valid, scale=scale)
+    out = sp_unpack(os_.view(P, B, N, Hl, D))
+    return out[:, :share.n_valid]
