@@ -11,8 +11,11 @@ ATTN_MEAN_ABS = 2e-3
 # absolute bars alone are loose): relative RMS error and cosine similarity.
 ATTN_REL_RMS = 1e-2
 ATTN_COSINE = 0.9999
-# Log-sum-exp is computed from fp32 scores and fp32 sums.
-LSE_ABS = 1e-3
+# Log-sum-exp: the kernel's row sum adds the bf16-rounded probabilities (the
+# same values that weight V), each within a relative 2^-9 of the exact one,
+# so the sum is within a relative 2^-9 and its log within ~2^-9 ~= 2e-3
+# (plus fp32 rounding, ~1e-6).  Bar: twice that.
+LSE_ABS = 4e-3
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

@@ -4,9 +4,12 @@
 // for its heads; padded keys are masked out).  bf16 inputs, bf16 matrix-core
 // products with fp32 accumulation, fp32 online softmax.
 //
-// Work split.  One workgroup = 4 waves = 128 query rows of one (batch, head);
-// each wave owns 32 query rows for the whole key loop.  Keys stream through
-// LDS in tiles of 64.  The whole query block is live in registers.
+// Work split.  One workgroup = 8 waves = 256 query rows of one (batch, head);
+// each wave owns 32 query rows for the whole key loop.  Two waves share each
+// SIMD, so one wave's softmax (VALU) runs while the other's matrix
+// instructions execute.  Keys stream through LDS in tiles of 64 keys,
+// double-buffered: while tile i is consumed, tile i+1 is copied global ->
+// LDS directly (buffer_load ... lds, no register staging).
 //
 // Matrix-core orientation.  v_mfma_f32_32x32x16_bf16 computes a 32x32 fp32
 // tile C += A(32x16) * B(16x32).  Lane l supplies row (l % 32) of A and
@@ -15,23 +18,33 @@
 // 8 * (r / 4) + 4 * (l / 32) + (r % 4) in accumulator register r.
 // The kernel computes the transposed score tile S^T = K * Q^T (A = 32 keys,
 // B = 32 queries), so every lane holds 16 scores of ONE query: the softmax
-// row statistics are mostly in-register, plus one exchange between the two
-// half-waves (ds_bpermute).  The output is likewise accumulated
-// transposed, O^T = V^T * P^T (A = 32 channels of V^T, B = P^T), so the
-// per-query rescale is a per-lane scalar.
+// row statistics are in-register plus one exchange between the two
+// half-waves (ds_bpermute).  The output is accumulated transposed too,
+// O^T = V^T * P^T (A = 32 channels of V^T, B = P^T), so the per-query
+// rescale is a per-lane scalar.
 //
-// Key order inside the P^T operand.  P^T comes straight from the S^T
-// accumulator: for 16 keys of a tile (registers 8j..8j+7 of one 32-key
-// block), lane half hf holds keys {4hf..4hf+3, 8+4hf..8+4hf+3} as its k
-// values 0..7.  The contraction index is only summed over, so V^T is stored
-// in LDS with its keys permuted the same way inside every 16-key group
-// (slot 8hf + e holds key 8(e/4) + 4hf + e%4); the A operand then is one
-// 16-byte LDS read.
+// P^T comes straight from the S^T accumulator: for the 16 keys held in
+// registers 8j..8j+7 of a 32-key tile, lane half hf holds keys
+// {4hf..4hf+3, 8+4hf..8+4hf+3} as its k values 0..7.  The V^T operand is read
+// in exactly that key order with two ds_read_b64_tr_b16, which transpose 4
+// rows x 16 columns of 16-bit values across each 16-lane group: lane j of a
+// group receives element j of each of the 4 rows.
 //
-// Masking.  Tiles wholly below nk_valid take no mask; the one tile that
-// straddles nk_valid sets the scores of keys >= nk_valid to -inf, and the
-// K/V loads of those keys are replaced by zeros, so no padded value
-// (NaN included) is read.  Tiles wholly at or past nk_valid are not visited.
+// LDS layout.  K and V tiles are row-major [64 keys][D] with the 16-byte
+// chunks of row r permuted by XOR with swz(r), so that the 32 rows read by
+// one K fragment and the 4 rows read by one V transpose read fall in
+// different banks.
+//
+// Softmax.  Scores are kept in the log2 domain (scale * log2 e folded into
+// one FMA before exp2).  The running max is only raised, and O and the row
+// sum rescaled, when a tile's max exceeds it by more than 8 (a factor of
+// 256); until then exp2 arguments stay <= 8, far from overflow.  The row sum
+// adds the bf16-rounded probabilities that also feed the P*V product.
+//
+// Masking.  Only the one tile that straddles nk_valid is masked (scores of
+// keys >= nk_valid set to -inf).  Its K/V rows past nk_valid are loaded from
+// row nk_valid-1 instead, so no padded value (NaN included) is ever read;
+// tiles wholly past nk_valid are not visited.
 #include <cmath>
 
 #include "common.h"
@@ -40,30 +53,70 @@
 namespace ltxa {
 namespace {
 
-constexpr int kWaves = 4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQW = 32;              // query rows per wave
-constexpr int kBQ = kWaves * kQW;    // query rows per workgroup
-constexpr int kBK = 64;              // keys per tile
+constexpr int kQW = 32;                // query rows per wave
+constexpr int kBQ = kWaves * kQW;      // query rows per workgroup
+constexpr int kBK = 64;                // keys per tile
+constexpr int kStages = 2;             // LDS ring depth
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
+// chips: 32-bit data format, everything else zero.
+constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt immediates for vmcnt(n), n = 0..15, with expcnt and lgkmcnt left
+// at their maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr short kWaitVm[16] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75, 0x0F76, 0x0F77,
+                               0x0F78, 0x0F79, 0x0F7A, 0x0F7B, 0x0F7C, 0x0F7D, 0x0F7E, 0x0F7F};
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Value of x held by lane l ^ 32 (the other half-wave, which holds the other
-// keys of the same query), through the LDS crossbar (ds_bpermute).
+// keys of the same query), through the LDS crossbar.
 __device__ __forceinline__ float partner(float x) {
   const int addr = ((__lane_id() ^ 32) << 2);
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
-__device__ __forceinline__ float halfwave_max(float x) { return fmaxf(x, partner(x)); }
-__device__ __forceinline__ float halfwave_sum(float x) { return x + partner(x); }
 
-// LDS slot of key kk (0..63) inside a V^T row: the 16-key groups keep their
-// place, inside a group the 4-key runs go in the order 0, 2, 1, 3.
-__device__ __forceinline__ int vt_slot(int kk) {
-  const int g = kk & ~15, w = kk & 15;
-  return g + 8 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
+// Chunk permutation of LDS row r (16-byte chunks).  D = 128: 16 chunks per
+// 256-byte row; rows 0..15 map one chunk to 16 distinct bank groups, and the
+// 4 consecutive rows of a transpose read to 4 distinct even offsets.
+// D = 64: 8 chunks per 128-byte row (two rows per 256-byte bank window).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return ((r & 7) << 1) ^ ((r >> 3) & 1);
+  else
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+// One 16-byte-per-lane copy global -> LDS through buffer resource r: lane l
+// reads byte offset voff and writes LDS bytes [dst + 16 l, +16).  (Kept out
+// of lambdas: inside one, this builtin stops the host-side launch stub from
+// being emitted.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, LDS_AS void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 template <int D>
@@ -71,16 +124,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
     int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2) {
-  constexpr int KS = D / 16;     // 16-channel steps of Q K^T
-  constexpr int DB = D / 32;     // 32-channel blocks of O^T
-  constexpr int KROW = D + 8;    // padded K row in LDS (elements)
-  constexpr int VROW = kBK + 8;  // padded V^T row in LDS (elements)
-  constexpr int CH = D / 8;      // 16-byte chunks per head row
-  constexpr int VK = D / 32;     // keys per thread in the tile load
-  static_assert(VK * (kThreads / CH) == kBK, "tile load covers the tile");
+  constexpr int KS = D / 16;            // 16-channel steps of K Q^T
+  constexpr int DB = D / 32;            // 32-channel blocks of O^T
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROW = D * 2;            // bytes per K/V row
+  constexpr int TILE = kBK * ROW;       // bytes per K or V tile
+  constexpr int LOADS = TILE / (kThreads * 16);  // DMA instructions per thread per tensor per tile
+  static_assert(LOADS * kThreads * 16 == TILE, "tile copy covers the tile");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kBK * KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[D * VROW];
+  // The ring: one LDS object per stage and tensor, so that the compiler can
+  // tell the stage being read from the stage being filled.
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE], sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE], sV1[TILE];
+
+  // Bytes a copy leaves unwritten must not hold stale NaN patterns: start
+  // the ring at zero.
+  {
+    char* const ring[4] = {sK0, sK1, sV0, sV1};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int off = threadIdx.x * 16; off < TILE; off += kThreads * 16)
+        *reinterpret_cast<u32x4*>(ring[i] + off) = u32x4{};
+  }
 
   const int lid = xcd_contiguous(blockIdx.x, nblocks);
   const int bh = lid / qblocks;
@@ -96,133 +162,172 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const __bf16* kbase = k + (b * nk_pad * heads + h) * D;
   const __bf16* vbase = v + (b * nk_pad * heads + h) * D;
 
-  // Q^T operand: this lane's query row, 8 channels per 16-channel step.
+  // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
   const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
   bf16x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (qrow < nq)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 16 + hf * 8);
-    else
-      qf[s] = bf16x8{};
+  for (int s = 0; s < KS; ++s)
+    qf[s] = qrow < nq ? *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 16 + hf * 8) : bf16x8{};
+
+  // Per-lane LDS offsets inside a tile.
+  // K fragment (S^T A operand) for step s: row ln (+32 for the second key
+  // block), chunk 2s + hf, stored at position (2s + hf) ^ swz(ln).
+  // V fragment for channel block d: two transpose reads; 16-lane group g,
+  // index gi inside it; rows 16G + 8r + 4(g/2) + gi/4, channels
+  // 32d + 16(g%2) + 4(gi%4).
+  int k_off[KS], v_off0[DB], v_off1[DB];
+  {
+    const int k_x = hf ^ swz<D>(ln);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k_off[s] = ln * ROW + (((2 * s) ^ k_x) << 4);
+    const int g = lane >> 4, gi = lane & 15;
+    const int v_row0 = 4 * (g >> 1) + (gi >> 2);
+    const int v_c = 2 * (g & 1) + ((gi & 3) >> 1);
+    const int v_x0 = v_c ^ swz<D>(v_row0);
+    const int v_x1 = v_c ^ swz<D>(v_row0 + 8);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      v_off0[d] = v_row0 * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x0) << 4);
+      v_off1[d] = (v_row0 + 8) * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x1) << 4);
+    }
   }
+
+  // Tile copy: DMA instruction j of this wave fills LDS bytes
+  // [(wave*LOADS + j) * 1024, +1024); lane l writes 16-byte slot
+  // s = (wave*LOADS + j)*64 + l = (row s / CH, position s % CH), which holds
+  // the row's global chunk (position ^ swz(row)).  The copy goes through a
+  // buffer resource whose extent ends with the last valid key: rows past it
+  // read as zeros, so the padded keys are never touched.
+  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
+  const int full_tiles = static_cast<int>(nk_valid / kBK);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t cp_off[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int s = (wave * LOADS + j) * 64 + lane;
+    const int row = s / CH;
+    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
+  }
+  auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
+    const int64_t first = int64_t(t) * kBK;
+    const int64_t rows = nk_valid - first < kBK ? nk_valid - first : kBK;
+    const uint32_t extent = static_cast<uint32_t>((rows - 1) * rs * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbase + first * rs, extent);
+    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbase + first * rs, extent);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + j) * 1024);
+      LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + j) * 1024);
+      dma16(rk, kd, cp_off[j]);
+      dma16(rv, vd, cp_off[j]);
+    }
+  };
 
   f32x16 acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
-  float m = -INFINITY;  // running max of scale*log2(e)*s
-  float l = 0.0f;       // running sum of exp2(.) over this lane's keys
+  float m = -INFINITY;  // running max (log2 domain) used as exp2 offset
+  float l = 0.0f;       // running sum over this lane's keys
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // Tile load mapping: thread -> 16-byte chunk `ch` of VK consecutive keys.
-  const int ch = tid % CH;
-  const int kg = tid / CH;
-  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
-
-  u32x4 kreg[VK], vreg[VK];
-  auto load_tile = [&](int t) {
+  auto compute_tile = [&] __device__(int t, const char* cK, const char* cV) __attribute__((always_inline)) {
+    const LDS_AS char* lK = (const LDS_AS char*)cK;
+    const LDS_AS char* lV = (const LDS_AS char*)cV;
+    // Keep the stage base out of the per-lane offsets (it is folded into
+    // each read's immediate offset instead of costing a register per stage).
 #pragma unroll
-    for (int i = 0; i < VK; ++i) {
-      const int64_t key = int64_t(t) * kBK + kg * VK + i;
-      if (key < nk_valid) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * rs + ch * 8);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + key * rs + ch * 8);
-      } else {
-        kreg[i] = u32x4{};
-        vreg[i] = u32x4{};
-      }
-    }
-  };
-  auto store_tile = [&]() {
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(k_off[s]));
 #pragma unroll
-    for (int i = 0; i < VK; ++i)
-      *reinterpret_cast<u32x4*>(&sK[(kg * VK + i) * KROW + ch * 8]) = kreg[i];
-    // Transpose VK keys x 8 channels into 8 channel rows of VK keys.
-    const int slot = vt_slot(kg * VK);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const bool hi = e & 1;
-      uint32_t words[VK / 2];
-#pragma unroll
-      for (int i = 0; i < VK / 2; ++i) {
-        const uint32_t a = vreg[2 * i][w], c = vreg[2 * i + 1][w];
-        words[i] = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-      }
-      __bf16* dstp = &sV[(ch * 8 + e) * VROW + slot];
-      if constexpr (VK == 4)
-        *reinterpret_cast<u32x2*>(dstp) = u32x2{words[0], words[1]};
-      else
-        *reinterpret_cast<uint32_t*>(dstp) = words[0];
-    }
-  };
-
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
-
-    // S^T = K * Q^T for two 32-key blocks.
+    for (int d = 0; d < DB; ++d) asm volatile("" : "+v"(v_off0[d]), "+v"(v_off1[d]));
+    // S^T = K * Q^T for the two 32-key blocks of the tile.
     f32x16 sc[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sc[mb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[(mb * 32 + ln) * KROW + s * 16 + hf * 8]);
-        sc[mb] = mfma32(kf, qf[s], sc[mb]);
+        const bf16x8 kf = *(const LDS_AS bf16x8*)(lK + kb * 32 * ROW + k_off[s]);
+        sc[kb] = mfma32(kf, qf[s], sc[kb]);
       }
     }
-
-    const int64_t tile0 = int64_t(t) * kBK;
-    if (tile0 + kBK > nk_valid) {
+    if (t >= full_tiles) {
+      // Key of register r in block kb is 32kb + 8(r/4) + 4hf + r%4: compare
+      // its lane-independent part against the lane's limit.
+      const int lim = static_cast<int>(nk_valid - int64_t(t) * kBK) - 4 * hf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = tile0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= nk_valid) sc[mb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
+    }
+    float a = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) a = fmaxf(a, fmaxf(sc[0][r], sc[1][r]));
+    const float mx = fmaxf(a, partner(a)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
     }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
-    mx = halfwave_max(mx);
-    const float m_new = fmaxf(m, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-
-    float psum = 0.0f;
+    // P^T in bf16, 16 keys per operand: operand (2kb + j) holds registers 8j..8j+7.
     bf16x8 pf[4];
+    const float nm = -m;
+    float sum = 0.0f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][8 * j + e], scale_log2, -m_new));
-          psum += p;
-          pf[2 * mb + j][e] = static_cast<__bf16>(p);
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e], scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e + 1], scale_log2, nm));
+          bf16x2 pp;
+          pp[0] = static_cast<__bf16>(p0);
+          pp[1] = static_cast<__bf16>(p1);
+          sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+          pf[2 * kb + j][e] = pp[0];
+          pf[2 * kb + j][e + 1] = pp[1];
         }
-    l = __builtin_fmaf(l, alpha, psum);
-#pragma unroll
-    for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+    l += sum;
 
     // O^T += V^T * P^T, one 16-key group at a time.
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int G = 0; G < 4; ++G)
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[(d * 32 + ln) * VROW + g * 16 + hf * 8]);
-        acc[d] = mfma32(vf, pf[g], acc[d]);
+        const LDS_AS char* p0 = lV + G * 16 * ROW + v_off0[d];
+        const LDS_AS char* p1 = lV + G * 16 * ROW + v_off1[d];
+        acc[d] = mfma32(lds_tr_pair(p0, p1), pf[G], acc[d]);
       }
+  };
+
+  char* const ringK[kStages] = {sK0, sK1};
+  char* const ringV[kStages] = {sV0, sV1};
+
+  // One iteration with the ring slot known at compile time: wait for tile t
+  // (stage ST), then copy tile t+1 into the other stage (which held tile
+  // t-1: every wave is done with it once past the barrier) and consume tile t.
+  auto iteration = [&] __device__(int t, auto st) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int S1 = (ST + 1) % kStages;
+    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);  // this thread's copies of tile t landed
+    __syncthreads();                         // everyone's
+    if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
+    compute_tile(t, ringK[ST], ringV[ST]);
+  };
+
+  issue_tile(0, ringK[0], ringV[0]);
+  for (int t = 0; t < ntiles; t += kStages) {
+    iteration(t, Int<0>{});
+    if (t + 1 >= ntiles) break;
+    iteration(t + 1, Int<1>{});
   }
 
-  const float lt = halfwave_sum(l);
+  const float lt = l + partner(l);
   if (qrow < nq) {
     const float inv = 1.0f / lt;
     __bf16* orow = o + (b * nq * heads + h) * D + qrow * rs;

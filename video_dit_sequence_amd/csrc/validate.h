@@ -117,6 +117,9 @@ inline int check_attn(const void* q, const void* k, const void* v, const void* o
   int64_t kb = mul4_capped(batch, nk_pad, heads, int64_t(head_dim) * 2);
   int64_t lb = mul4_capped(batch, heads, nq, 4);
   if (qb < 0 || kb < 0 || lb < 0) return LTXA_E_RANGE;
+  // Per-tile element offsets inside the kernel are 32-bit: 64 token rows of
+  // heads * head_dim elements must stay below 2^31.
+  if (int64_t(heads) * head_dim * 64 >= (INT64_C(1) << 31)) return LTXA_E_RANGE;
   // Grid x = ceil(nq / rows per block) * batch * heads must stay below 2^31.
   int64_t qblocks = (nq + 63) / 64;
   if (mul_capped(qblocks, mul_capped(batch, heads)) < 0 ||
