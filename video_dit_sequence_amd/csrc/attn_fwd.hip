@@ -64,6 +64,13 @@ constexpr int kBQ = kWaves * kQW;      // query rows per workgroup
 constexpr int kBK = 64;                // keys per tile
 constexpr int kStages = 2;             // LDS ring depth
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kKAhead = 3;        // K fragments in flight ahead of the products
+constexpr int kVAhead = 2;        // V fragments in flight ahead of the products
+constexpr int kValuPerGroup = 24; // VALU ops per 16-key group of probabilities
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // chips: 32-bit data format, everything else zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -90,13 +97,15 @@ __device__ __forceinline__ float partner(float x) {
 }
 
 // Chunk permutation of LDS row r (16-byte chunks).  D = 128: 16 chunks per
-// 256-byte row; rows 0..15 map one chunk to 16 distinct bank groups, and the
-// 4 consecutive rows of a transpose read to 4 distinct even offsets.
+// 256-byte row; the 16 rows r..r+15 of a K fragment read put one chunk in 16
+// distinct positions, and the 4 consecutive rows of a V transpose read
+// (which take 2 adjacent chunks each) land 4 positions apart.  Measured on
+// MI355X with SQ_LDS_BANK_CONFLICT: zero conflict cycles for both reads.
 // D = 64: 8 chunks per 128-byte row (two rows per 256-byte bank window).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128)
-    return ((r & 7) << 1) ^ ((r >> 3) & 1);
+    return ((r & 3) << 2) | ((r >> 2) & 3);
   else
     return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
@@ -230,7 +239,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   float l = 0.0f;       // running sum over this lane's keys
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  auto compute_tile = [&] __device__(int t, const char* cK, const char* cV) __attribute__((always_inline)) {
+  auto compute_tile = [&] __device__(int t, const char* cK, const char* cV, auto masked)
+                          __attribute__((always_inline)) {
     const LDS_AS char* lK = (const LDS_AS char*)cK;
     const LDS_AS char* lV = (const LDS_AS char*)cV;
     // Keep the stage base out of the per-lane offsets (it is folded into
@@ -239,18 +249,26 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(k_off[s]));
 #pragma unroll
     for (int d = 0; d < DB; ++d) asm volatile("" : "+v"(v_off0[d]), "+v"(v_off1[d]));
-    // S^T = K * Q^T for the two 32-key blocks of the tile.
-    f32x16 sc[2];
+    // S^T = K * Q^T for the two 32-key blocks of the tile.  Fragment i feeds
+    // block i % 2 at channel step i / 2, so consecutive products are
+    // independent; reads run kKAhead fragments ahead of the products.
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    {
+      bf16x8 kf[2 * KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
+      for (int i = 0; i < 2 * KS; ++i)
+        kf[i] = *(const LDS_AS bf16x8*)(lK + (i & 1) * 32 * ROW + k_off[i >> 1]);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *(const LDS_AS bf16x8*)(lK + kb * 32 * ROW + k_off[s]);
-        sc[kb] = mfma32(kf, qf[s], sc[kb]);
+      for (int i = 0; i < 2 * KS; ++i) sc[i & 1] = mfma32(kf[i], qf[i >> 1], sc[i & 1]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS - kKAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKAhead, 0);
     }
-    if (t >= full_tiles) {
+    if constexpr (decltype(masked)::value != 0) {
       // Key of register r in block kb is 32kb + 8(r/4) + 4hf + r%4: compare
       // its lane-independent part against the lane's limit.
       const int lim = static_cast<int>(nk_valid - int64_t(t) * kBK) - 4 * hf;
@@ -273,36 +291,50 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       for (int d = 0; d < DB; ++d) acc[d] *= alpha;
     }
 
-    // P^T in bf16, 16 keys per operand: operand (2kb + j) holds registers 8j..8j+7.
-    bf16x8 pf[4];
+    // P^T in bf16, 16 keys per operand: operand (2kb + j) holds registers
+    // 8j..8j+7 of block kb.  O^T += V^T * P^T one 16-key group at a time.
+    // Order: the exponentials of group G+1 are interleaved with the four
+    // products of group G, and V fragments are read two products ahead.
     const float nm = -m;
     float sum = 0.0f;
+    auto probs = [&] __device__(int G) __attribute__((always_inline)) {
+      bf16x8 pg;
+      const int kb = G >> 1, j = G & 1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e], scale_log2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e + 1], scale_log2, nm));
-          bf16x2 pp;
-          pp[0] = static_cast<__bf16>(p0);
-          pp[1] = static_cast<__bf16>(p1);
-          sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
-          pf[2 * kb + j][e] = pp[0];
-          pf[2 * kb + j][e + 1] = pp[1];
-        }
-    l += sum;
-
-    // O^T += V^T * P^T, one 16-key group at a time.
-#pragma unroll
-    for (int G = 0; G < 4; ++G)
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const LDS_AS char* p0 = lV + G * 16 * ROW + v_off0[d];
-        const LDS_AS char* p1 = lV + G * 16 * ROW + v_off1[d];
-        acc[d] = mfma32(lds_tr_pair(p0, p1), pf[G], acc[d]);
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e], scale_log2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e + 1], scale_log2, nm));
+        bf16x2 pp;
+        pp[0] = static_cast<__bf16>(p0);
+        pp[1] = static_cast<__bf16>(p1);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+        pg[e] = pp[0];
+        pg[e + 1] = pp[1];
       }
+      return pg;
+    };
+    bf16x8 pf[4];
+    bf16x8 vf[4 * DB];
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      const int G = i / DB, d = i % DB;
+      vf[i] = lds_tr_pair(lV + G * 16 * ROW + v_off0[d], lV + G * 16 * ROW + v_off1[d]);
+    }
+#pragma unroll
+    for (int G = 0; G < 4; ++G) pf[G] = probs(G);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) acc[i % DB] = mfma32(vf[i], pf[i / DB], acc[i % DB]);
+    l += sum;
+    // Schedule: P(0) and the first reads, then per product: 1 MFMA, the next
+    // fragment's 2 transpose reads, and a share of the next group's exps.
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerGroup, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVAhead, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+      if (i + kVAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      if (i < 3 * DB) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerGroup / DB, 1);
+    }
   };
 
   char* const ringK[kStages] = {sK0, sK1};
@@ -311,20 +343,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   // One iteration with the ring slot known at compile time: wait for tile t
   // (stage ST), then copy tile t+1 into the other stage (which held tile
   // t-1: every wave is done with it once past the barrier) and consume tile t.
-  auto iteration = [&] __device__(int t, auto st) __attribute__((always_inline)) {
+  auto iteration = [&] __device__(int t, auto st, auto masked) __attribute__((always_inline)) {
     constexpr int ST = decltype(st)::value;
     constexpr int S1 = (ST + 1) % kStages;
     __builtin_amdgcn_s_waitcnt(kWaitVm[0]);  // this thread's copies of tile t landed
     __syncthreads();                         // everyone's
     if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
-    compute_tile(t, ringK[ST], ringV[ST]);
+    compute_tile(t, ringK[ST], ringV[ST], masked);
   };
 
+  // Steady state: pairs of wholly valid tiles, no masking.  Then at most one
+  // more full tile and the one tile that straddles nk_valid.
   issue_tile(0, ringK[0], ringV[0]);
-  for (int t = 0; t < ntiles; t += kStages) {
-    iteration(t, Int<0>{});
-    if (t + 1 >= ntiles) break;
-    iteration(t + 1, Int<1>{});
+  int t = 0;
+  for (; t + 2 <= full_tiles; t += 2) {
+    iteration(t, Int<0>{}, Int<0>{});
+    iteration(t + 1, Int<1>{}, Int<0>{});
+  }
+  if (t < full_tiles) {
+    iteration(t, Int<0>{}, Int<0>{});
+    if (t + 1 < ntiles) iteration(t + 1, Int<1>{}, Int<1>{});
+  } else if (t < ntiles) {
+    iteration(t, Int<0>{}, Int<1>{});
   }
 
   const float lt = l + partner(l);
