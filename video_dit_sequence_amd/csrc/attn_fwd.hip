@@ -35,11 +35,13 @@
 // one K fragment and the 4 rows read by one V transpose read fall in
 // different banks.
 //
-// Softmax.  Scores are kept in the log2 domain (scale * log2 e folded into
-// one FMA before exp2).  The running max is only raised, and O and the row
-// sum rescaled, when a tile's max exceeds it by more than 8 (a factor of
-// 256); until then exp2 arguments stay <= 8, far from overflow.  The row sum
-// adds the bf16-rounded probabilities that also feed the P*V product.
+// Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once),
+// so the products are log2-domain scores, and every score product starts
+// from a register block holding -m: exp2 consumes the accumulator as is.
+// The running max m is only raised, and O and the row sum rescaled, when a
+// tile's max exceeds it by more than 8 (a factor of 256); until then exp2
+// arguments stay <= 8, far from overflow.  The row sum adds the
+// bf16-rounded probabilities that also feed the P*V product.
 //
 // Masking.  Only the one tile that straddles nk_valid is masked (scores of
 // keys >= nk_valid set to -inf).  Its K/V rows past nk_valid are loaded from
@@ -70,7 +72,7 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kKAhead = 3;        // K fragments in flight ahead of the products
 constexpr int kVAhead = 2;        // V fragments in flight ahead of the products
-constexpr int kValuPerGroup = 24; // VALU ops per 16-key group of probabilities
+constexpr int kValuPerGroup = 16; // VALU ops per 16-key group of probabilities
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // chips: 32-bit data format, everything else zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -173,10 +175,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 
   // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
   const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
+  // Q is multiplied by scale * log2(e) once here (rounded back to bf16), so
+  // that the products are already log2-domain scores.
   bf16x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qf[s] = qrow < nq ? *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 16 + hf * 8) : bf16x8{};
+  for (int s = 0; s < KS; ++s) {
+    bf16x8 x = qrow < nq ? *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 16 + hf * 8) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * scale_log2);
+    qf[s] = x;
+  }
 
   // Per-lane LDS offsets inside a tile.
   // K fragment (S^T A operand) for step s: row ln (+32 for the second key
@@ -235,8 +243,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   f32x16 acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
-  float m = -INFINITY;  // running max (log2 domain) used as exp2 offset
+  // Softmax state.  m is the offset subtracted from every log2-domain score
+  // before exp2; it is the running max, raised only when a tile exceeds it
+  // by more than kRescaleSlack.  The score products start from a register
+  // block holding -m, so they come out already offset (no per-score VALU).
+  float m = 0.0f;       // replaced by the first tile's max
   float l = 0.0f;       // running sum over this lane's keys
+  f32x16 neg_m = f32x16{};
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   auto compute_tile = [&] __device__(int t, const char* cK, const char* cV, auto masked)
@@ -252,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     // S^T = K * Q^T for the two 32-key blocks of the tile.  Fragment i feeds
     // block i % 2 at channel step i / 2, so consecutive products are
     // independent; reads run kKAhead fragments ahead of the products.
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 sc[2] = {neg_m, neg_m};
     {
       bf16x8 kf[2 * KS];
 #pragma unroll
@@ -281,29 +294,38 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     float a = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) a = fmaxf(a, fmaxf(sc[0][r], sc[1][r]));
-    const float mx = fmaxf(a, partner(a)) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
+    const float mx = fmaxf(a, partner(a));  // tile max, relative to m
+    if (__builtin_amdgcn_ballot_w64(t == 0 || mx > kRescaleSlack)) {
+      // First tile: m becomes its max.  Later: raise m to the new max (when
+      // above it) and rescale what has been accumulated.
+      const float delta = t == 0 ? mx : fmaxf(mx, 0.0f);
+      if (t != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        l *= alpha;
 #pragma unroll
-      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+        for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+      }
+      m += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[0][r] -= delta;
+        sc[1][r] -= delta;
+        neg_m[r] = -m;
+      }
     }
 
     // P^T in bf16, 16 keys per operand: operand (2kb + j) holds registers
     // 8j..8j+7 of block kb.  O^T += V^T * P^T one 16-key group at a time.
     // Order: the exponentials of group G+1 are interleaved with the four
     // products of group G, and V fragments are read two products ahead.
-    const float nm = -m;
     float sum = 0.0f;
     auto probs = [&] __device__(int G) __attribute__((always_inline)) {
       bf16x8 pg;
       const int kb = G >> 1, j = G & 1;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e], scale_log2, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * j + e + 1], scale_log2, nm));
+        const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e + 1]);
         bf16x2 pp;
         pp[0] = static_cast<__bf16>(p0);
         pp[1] = static_cast<__bf16>(p1);
