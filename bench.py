@@ -7,9 +7,14 @@ every rank's 4 heads, and unpack the output.  Every part is exactly 8x one
 rank's share, so the rate equals one rank's.  Inputs are seeded synthetic
 bf16 N(0,1) tensors already resident in HBM.
 
+The default path takes four launches (``--path fused``): Q and K are packed
+and rotated in one pass each, V is packed, and the attention kernel writes
+its output in token order.  ``--path unfused`` times the six-launch sequence
+(pack x3, rotary, attention, unpack); both compute the same bits.
+
 Prints one JSON line.  ``value`` is attention TFLOP/s over the whole step
 (4 * Nq * Nk_valid * D * H flop per step).  ``roofline`` covers the dominant
-kernel (ltxa_attn_fwd), timed with HIP events on its own stream inside the
+kernel (attn_fwd_kernel, launched by ltxa_attn_fwd_unpack or ltxa_attn_fwd), timed with HIP events on its own stream inside the
 timed region.  ``cpu_baseline`` is the fp64 numpy oracle on a bounded row
 sample of the same workload.
 """
@@ -37,6 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 skips it)")
     return ap.parse_args()
@@ -129,23 +135,41 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    if args.path == "fused":
+        phase_names = ("pack_rope_qk", "pack_v", "attn_fwd")
+
+        def launches():
+            ltxa.sp_pack_rope(q, pos, w.q_max_pos, P, w.theta, out=qs)
+            yield ltxa.sp_pack_rope(k, pos, w.k_max_pos, P, w.theta, out=ks)
+            yield ltxa.sp_pack(v, P, out=vs)
+            yield ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=out)
+    else:
+        phase_names = ("pack_qkv", "rope_qk", "attn_fwd", "unpack_o")
+
+        def launches():
+            ltxa.sp_pack(q, P, out=qs)
+            ltxa.sp_pack(k, P, out=ks)
+            yield ltxa.sp_pack(v, P, out=vs)
+            yield ltxa.rope_qk(qs.view(P * B, N, Hl, D), pos, w.q_max_pos, ks.view(P * B, N, Hl, D),
+                               pos, w.k_max_pos, w.theta)
+            yield ltxa.attn_fwd(qs.view(P * B, N, Hl, D), ks.view(P * B, N, Hl, D),
+                                vs.view(P * B, N, Hl, D), nk_valid=w.nk_valid,
+                                out=os_.view(P * B, N, Hl, D))
+            yield ltxa.sp_unpack(os_, out=out)
+
     def step(record=None):
-        marks = [ev() for _ in range(5)] if record is not None else None
-        if marks: marks[0].record(stream)
-        ltxa.sp_pack(q, P, out=qs)
-        ltxa.sp_pack(k, P, out=ks)
-        ltxa.sp_pack(v, P, out=vs)
-        if marks: marks[1].record(stream)
-        ltxa.rope_qk(qs.view(P * B, N, Hl, D), pos, w.q_max_pos, ks.view(P * B, N, Hl, D), pos,
-                     w.k_max_pos, w.theta)
-        if marks: marks[2].record(stream)
-        ltxa.attn_fwd(qs.view(P * B, N, Hl, D), ks.view(P * B, N, Hl, D), vs.view(P * B, N, Hl, D),
-                      nk_valid=w.nk_valid, out=os_.view(P * B, N, Hl, D))
-        if marks: marks[3].record(stream)
-        ltxa.sp_unpack(os_, out=out)
-        if marks: marks[4].record(stream)
-        if record is not None:
-            record.append(marks)
+        # One event before the step and one after each phase, all on the
+        # stream the kernels are launched on.
+        if record is None:
+            for _ in launches():
+                pass
+            return
+        marks = [ev()]
+        marks[0].record(stream)
+        for _ in launches():
+            marks.append(ev())
+            marks[-1].record(stream)
+        record.append(marks)
 
     for _ in range(args.warmup):
         step()
@@ -158,7 +182,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    phases = {"pack_qkv": [], "rope_qk": [], "attn_fwd": [], "unpack_o": []}
+    phases = {name: [] for name in phase_names}
     for m in records:
         for i, name in enumerate(phases):
             phases[name].append(m[i].elapsed_time(m[i + 1]))
@@ -168,9 +192,14 @@ def main():
     step_tflops = attn_flop / (ms_per_step * 1e-3) / 1e12
     attn_tflops = attn_flop / (avg["attn_fwd"] * 1e-3) / 1e12
     traffic = traffic_per_launch()
-    pack_bytes = 3 * 2.0 * B * N * H * D * 2
-    unpack_bytes = 2.0 * B * N * H * D * 2
-    rope_bytes = 2 * 2.0 * B * N * H * D * 2 + N * 3 * 4
+    tensor_bytes = 2.0 * B * N * H * D                  # one bf16 [B, N, H, D] tensor
+    phase_bytes = {                                     # algorithmic HBM bytes (read + write)
+        "pack_rope_qk": 2 * 2 * tensor_bytes + 2 * N * 3 * 4,
+        "pack_v": 2 * tensor_bytes,
+        "pack_qkv": 3 * 2 * tensor_bytes,
+        "rope_qk": 2 * 2 * tensor_bytes + 2 * N * 3 * 4,
+        "unpack_o": 2 * tensor_bytes,
+    }
 
     line = {
         "metric": METRIC,
@@ -187,17 +216,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "tokens": N, "valid_tokens": w.nq_valid, "heads": H,
                    "head_dim": D, "virtual_ranks": P, "heads_per_rank": Hl, "batch": B,
-                   "grid_txy": list(w.q_grid), "rope_theta": w.theta},
+                   "grid_txy": list(w.q_grid), "rope_theta": w.theta, "path": args.path},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "ltxa_attn_fwd",
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128>",
                      "flop_per_launch": attn_flop, "avg_launch_ms": round(avg["attn_fwd"], 4)},
         "phases_ms": {k_: round(x, 4) for k_, x in avg.items()},
-        "hbm_GBps": {
-            "pack_qkv": round(pack_bytes / (avg["pack_qkv"] * 1e-3) / 1e9, 1),
-            "rope_qk": round(rope_bytes / (avg["rope_qk"] * 1e-3) / 1e9, 1),
-            "unpack_o": round(unpack_bytes / (avg["unpack_o"] * 1e-3) / 1e9, 1),
-            "peak": PEAK_HBM_GBS},
+        "hbm_GBps": {**{k_: round(phase_bytes[k_] / (avg[k_] * 1e-3) / 1e9, 1)
+                        for k_ in phase_names if k_ in phase_bytes}, "peak": PEAK_HBM_GBS},
         "device": torch.cuda.get_device_name(0),
     }
     if args.cpu_seconds > 0:

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 100 /* major*100 + minor */
+#define LTXA_VERSION 101 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -145,6 +145,54 @@ int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
 int ltxa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
                   int64_t nk_pad, int64_t nk_valid, float scale, void* stream);
+
+/*
+ * ltxa_sp_pack_rope -- ltxa_sp_pack and the rotary embedding of
+ * ltxa_rope_qk in one pass over memory (the SP page's exchange of Q or K,
+ * "What it is", followed by the FastVideo gemma page's
+ * apply_ltx_rotary_emb; the rotation acts per token and per pair, so it
+ * commutes with the head permutation).
+ *
+ *   src: bf16 [batch, n_tokens, heads, head_dim], read only.
+ *   dst: bf16 [world_size, batch, n_tokens, heads/world_size, head_dim]:
+ *     dst[p][b][n][j] = rotate(src[b][n][p*(heads/world_size) + j], pos[n]).
+ *   pos: DEVICE int32 [n_tokens, axes]; max_pos: HOST array of `axes`
+ *     values; theta: frequency base.  The angle schedule, the arithmetic and
+ *     the rounding are those of ltxa_rope_qk, so dst equals, bit for bit,
+ *     ltxa_sp_pack followed by ltxa_rope_qk on the packed tensor (positions
+ *     shared by every rank).
+ * Errors: E_NULL (src, dst, pos or max_pos NULL); E_SHAPE (as ltxa_rope_qk
+ * for sizes, axes, max_pos and theta; world_size < 1); E_DIVISIBILITY (as
+ * ltxa_sp_pack); E_ALIGN (src, dst or pos not 16-byte aligned, or
+ * head_dim*2 not a multiple of 16); E_ALIAS (src and dst overlap); E_RANGE.
+ */
+int ltxa_sp_pack_rope(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
+                      int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                      int32_t head_dim, int32_t world_size, double theta, void* stream);
+
+/*
+ * ltxa_attn_fwd_unpack -- ltxa_attn_fwd on every rank's head shard with the
+ * output written straight into token order (SP page, "What it is": each rank
+ * attends over all tokens for its heads, then results are shuffled back).
+ *
+ *   q: bf16 [world_size, batch, nq, heads/world_size, head_dim]
+ *   k, v: bf16 [world_size, batch, nk_pad, heads/world_size, head_dim]
+ *     (the layout ltxa_sp_pack / ltxa_sp_pack_rope write).
+ *   o: bf16 [batch, nq, heads, head_dim] (written): rank p's head j lands at
+ *     head p*(heads/world_size) + j.
+ *   lse: fp32 [world_size, batch, heads/world_size, nq], or NULL.
+ *   batch and heads are the unsharded counts.  Masking, scale and
+ *   arithmetic are those of ltxa_attn_fwd; o equals, bit for bit,
+ *   ltxa_attn_fwd over the world_size * batch shard entries followed by
+ *   ltxa_sp_unpack.
+ * Errors: those of ltxa_attn_fwd for world_size * batch entries of
+ * heads/world_size heads; E_SHAPE (world_size < 1); E_DIVISIBILITY
+ * (heads % world_size != 0).
+ */
+int ltxa_attn_fwd_unpack(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                         int64_t nk_pad, int64_t nk_valid, float scale, int32_t world_size,
+                         void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

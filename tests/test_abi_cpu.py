@@ -125,6 +125,43 @@ def test_attn_errors(L):
     assert f(A, B, C, D_, None, 1 << 30, 1 << 10, 128, 1 << 20, 1 << 20, 1, 0.1, None) == ltxa.LTXA_E_RANGE
 
 
+def test_pack_rope_errors(L):
+    f = L.ltxa_sp_pack_rope
+    mp3 = _mp(3, 7, 11)
+    # src, dst, pos, n, axes, max_pos, batch, heads, head_dim, world_size, theta
+    assert f(None, B, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, None, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, None, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, 232, 3, None, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, 232, 3, mp3, 0, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 3, mp3, 1, 4, 64, 0, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 3, mp3, 1, 4, 63, 2, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 4, _mp(1, 1, 1, 1), 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 3, mp3, 1, 4, 64, 2, -1.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 0, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 3, mp3, 1, 6, 64, 4, 1e4, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, C, 231, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, C, 232, 3, mp3, 1, 4, 4, 2, 1e4, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B + 8, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C + 4, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, A + 256, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, None) == ltxa.LTXA_E_ALIAS
+
+
+def test_attn_unpack_errors(L):
+    f = L.ltxa_attn_fwd_unpack
+    good = (1, 8, 128, 232, 232, 231, 0.088)
+    assert f(None, B, C, D_, None, *good, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, None, None, *good, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, D_, None, *good, 0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, *good, 3, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, C, D_, None, 1, 8, 96, 232, 232, 231, 0.1, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 8, 128, 232, 232, 0, 0.1, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A + 8, B, C, D_, None, *good, 2, None) == ltxa.LTXA_E_ALIGN
+    # o spans world_size * batch * nq * (heads/world_size) rows, as q does.
+    assert f(A, B, C, A + 64, None, *good, 2, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, D_, None, 1 << 40, 1 << 13, 128, 232, 232, 231, 0.1, 1 << 13, None) == ltxa.LTXA_E_RANGE
+
+
 def test_sp_share_bookkeeping():
     s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096

@@ -43,6 +43,10 @@
 // arguments stay <= 8, far from overflow.  The row sum adds the
 // bf16-rounded probabilities that also feed the P*V product.
 //
+// Output.  Staged per wave through LDS and stored as whole rows (see the
+// end of the kernel); the row addressing also lets the output land directly
+// in the token-major layout the head shards came from.
+//
 // Masking.  Only the one tile that straddles nk_valid is masked (scores of
 // keys >= nk_valid set to -inf).  Its K/V rows past nk_valid are loaded from
 // row nk_valid-1 instead, so no padded value (NaN included) is ever read;
@@ -134,7 +138,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
-    int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2) {
+    int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
+    int32_t out_heads) {
   constexpr int KS = D / 16;            // 16-channel steps of K Q^T
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
   constexpr int CH = D / 8;             // 16-byte chunks per row
@@ -172,6 +177,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const __bf16* qbase = q + (b * nq * heads + h) * D;
   const __bf16* kbase = k + (b * nk_pad * heads + h) * D;
   const __bf16* vbase = v + (b * nk_pad * heads + h) * D;
+  // Output slot of (b, h): head (b / out_batch) * heads + h of output batch
+  // entry b % out_batch, out_heads heads per token (the operands' own layout
+  // when out_batch is the batch and out_heads the head count).  b < 2^31 by
+  // the grid limit.  Both output pointers are formed here and pinned, so
+  // that their kernel-argument loads complete before the key loop instead
+  // of staying in flight (and being waited on) inside it.
+  const int32_t ob = static_cast<int32_t>(b) % out_batch, op = static_cast<int32_t>(b) / out_batch;
+  __bf16* obase = o + ((int64_t(ob) * nq * out_heads) + int64_t(op) * heads + h) * D;
+  float* lbase = lse ? lse + (b * heads + h) * nq : nullptr;
+  asm volatile("" : "+s"(obase), "+s"(lbase));
+  const int64_t ors = int64_t(out_heads) * D;  // elements between output tokens
 
   // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
   const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
@@ -390,25 +406,46 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   }
 
   const float lt = l + partner(l);
-  if (qrow < nq) {
-    const float inv = 1.0f / lt;
-    __bf16* orow = o + (b * nq * heads + h) * D + qrow * rs;
+  const float inv = 1.0f / lt;
+  if (lbase && hf == 0 && qrow < nq) lbase[qrow] = (m + __builtin_log2f(lt)) * 0.69314718055994531f;
+
+  // Output.  A lane holds 4-channel pieces of one query row, so storing
+  // them directly would scatter 8-byte writes over 32 rows per instruction;
+  // with a wide token stride (the unpacked layout) the L2 then writes lines
+  // back half-filled.  Instead each wave stages its 32 x D tile in LDS (the
+  // ring is free once every wave has left the key loop), row-major with the
+  // 16-byte chunks of row r permuted by XOR with r % CH, and writes whole
+  // rows: 16 bytes per lane, 64 / CH rows per instruction.
+  static_assert(2 * kQW == kBK, "two waves' output tiles fill one ring stage");
+  __syncthreads();
+  char* const stage = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sV0 : sV1) + (wave & 1) * (kQW * ROW);
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+  for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const u32x2 w = {pack_bf16x2(acc[d][4 * rg] * inv, acc[d][4 * rg + 1] * inv),
-                         pack_bf16x2(acc[d][4 * rg + 2] * inv, acc[d][4 * rg + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d * 32 + 8 * rg + 4 * hf) = w;
-      }
-    if (lse && hf == 0) lse[(b * heads + h) * nq + qrow] = (m + __builtin_log2f(lt)) * 0.69314718055994531f;
+    for (int rg = 0; rg < 4; ++rg) {
+      const u32x2 w = {pack_bf16x2(acc[d][4 * rg] * inv, acc[d][4 * rg + 1] * inv),
+                       pack_bf16x2(acc[d][4 * rg + 2] * inv, acc[d][4 * rg + 3] * inv)};
+      const int c = 4 * d + rg;  // 16-byte chunk: channels 8c .. 8c + 7; this half holds 4hf .. 4hf + 3
+      *reinterpret_cast<u32x2*>(stage + ln * ROW + ((c ^ (ln % CH)) << 4) + hf * 8) = w;
+    }
+  __syncthreads();
+  constexpr int RPI = 64 / CH;  // rows per store instruction
+  const int64_t q0 = int64_t(qb) * kBQ + wave * kQW;
+#pragma unroll
+  for (int i = 0; i < kQW / RPI; ++i) {
+    const int r = i * RPI + lane / CH, c = lane % CH;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * ROW + ((c ^ (r % CH)) << 4));
+    if (q0 + r < nq) *reinterpret_cast<u32x4*>(obase + (q0 + r) * ors + c * 8) = w;
   }
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch,
                     int32_t heads, int64_t nq, int64_t nk_pad, int64_t nk_valid, float scale,
-                    hipStream_t stream) {
+                    int64_t out_batch, int32_t out_heads, hipStream_t stream) {
+  if (out_batch < 1 || out_batch > batch || batch % out_batch != 0 ||
+      int64_t(out_heads) != (batch / out_batch) * heads)
+    return hipErrorInvalidValue;
   (void)hipGetLastError();  // report only this launch's error
   const int64_t qblocks = (nq + kBQ - 1) / kBQ;
   const int64_t nblocks = qblocks * batch * heads;
@@ -417,7 +454,8 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(static_cast<uint32_t>(nblocks)), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nq, nk_pad, nk_valid,
-                     heads, static_cast<int32_t>(qblocks), static_cast<int32_t>(nblocks), scale_log2);
+                     heads, static_cast<int32_t>(qblocks), static_cast<int32_t>(nblocks), scale_log2,
+                     static_cast<int32_t>(out_batch), out_heads);
   return hipGetLastError();
 }
 
@@ -425,10 +463,13 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk_pad,
-                       int64_t nk_valid, float scale, hipStream_t stream) {
+                       int64_t nk_valid, float scale, int64_t out_batch, int32_t out_heads,
+                       hipStream_t stream) {
   if (head_dim == 128)
-    return launch_d<128>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, stream);
-  return launch_d<64>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, stream);
+    return launch_d<128>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, out_batch, out_heads,
+                         stream);
+  return launch_d<64>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, out_batch, out_heads,
+                      stream);
 }
 
 }  // namespace ltxa

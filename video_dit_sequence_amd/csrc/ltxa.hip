@@ -100,5 +100,29 @@ LTXA_EXPORT int ltxa_attn_fwd(const void* q, const void* k, const void* v, void*
   const int rc = ltxa::check_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid, scale);
   if (rc) return rc;
   return launch_status(ltxa::launch_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid,
-                                         scale, static_cast<hipStream_t>(stream)));
+                                         scale, batch, heads, static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_sp_pack_rope(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
+                                  int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                                  int32_t head_dim, int32_t world_size, double theta, void* stream) {
+  const int rc = ltxa::check_pack_rope(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim,
+                                       world_size, theta);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_pack_rope(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
+                                              pos, n_tokens, axes, batch, heads, head_dim, world_size,
+                                              rope_table(head_dim, axes, max_pos, theta),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_attn_fwd_unpack(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                                     int64_t nk_pad, int64_t nk_valid, float scale, int32_t world_size,
+                                     void* stream) {
+  const int rc = ltxa::check_attn_unpack(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid,
+                                         scale, world_size);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_attn(q, k, v, o, lse, batch * world_size, heads / world_size, head_dim,
+                                         nq, nk_pad, nk_valid, scale, batch, heads,
+                                         static_cast<hipStream_t>(stream)));
 }

@@ -132,4 +132,41 @@ inline int check_attn(const void* q, const void* k, const void* v, const void* o
   return LTXA_OK;
 }
 
+// Fused pack + rotary: src [batch, n_tokens, heads, head_dim] bf16 ->
+// dst [world_size, batch, n_tokens, heads/world_size, head_dim] bf16.
+inline int check_pack_rope(const void* src, const void* dst, const int32_t* pos, int64_t n_tokens,
+                           int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                           int32_t head_dim, int32_t world_size, double theta) {
+  if (!src || !dst) return LTXA_E_NULL;
+  if (batch < 1 || heads < 1 || world_size < 1) return LTXA_E_SHAPE;
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2 != 0) return LTXA_E_SHAPE;
+  if (!(std::isfinite(theta) && theta > 0.0)) return LTXA_E_SHAPE;
+  if ((head_dim * 2) % 16 != 0) return LTXA_E_ALIGN;
+  int rc = check_rope_tensor(src, pos, n_tokens, axes, max_pos, head_dim);
+  if (rc) return rc;
+  if (!aligned16(dst)) return LTXA_E_ALIGN;
+  if (heads % world_size != 0 || n_tokens % world_size != 0) return LTXA_E_DIVISIBILITY;
+  const int64_t bytes = mul4_capped(batch, n_tokens, heads, int64_t(head_dim) * 2);
+  if (bytes < 0 || mul_capped(n_tokens, axes) < 0) return LTXA_E_RANGE;
+  if (n_tokens > (INT64_C(1) << 40)) return LTXA_E_RANGE;
+  if (overlap(src, bytes, dst, bytes)) return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
+// Attention over world_size head shards [world_size, batch, n, heads/world_size,
+// head_dim] with the output in the token-major [batch, nq, heads, head_dim]
+// layout: the same checks as check_attn over a batch of world_size * batch
+// entries with heads/world_size heads each.
+inline int check_attn_unpack(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, int64_t batch, int32_t heads, int32_t head_dim,
+                             int64_t nq, int64_t nk_pad, int64_t nk_valid, float scale,
+                             int32_t world_size) {
+  if (!q || !k || !v || !o) return LTXA_E_NULL;
+  if (batch < 1 || heads < 1 || world_size < 1) return LTXA_E_SHAPE;
+  if (heads % world_size != 0) return LTXA_E_DIVISIBILITY;
+  if (mul_capped(batch, world_size) < 0) return LTXA_E_RANGE;
+  return check_attn(q, k, v, o, lse, batch * world_size, heads / world_size, head_dim, nq, nk_pad,
+                    nk_valid, scale);
+}
+
 }  // namespace ltxa

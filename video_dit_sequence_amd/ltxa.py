@@ -34,7 +34,7 @@ LTXA_E_HIP = -6
 LTXA_E_RANGE = -7
 
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
-           "ltxa_rope_qk", "ltxa_attn_fwd")
+           "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack")
 
 
 class LtxaError(RuntimeError):
@@ -71,6 +71,12 @@ def lib() -> ctypes.CDLL:
         L.ltxa_attn_fwd.restype = ctypes.c_int
         L.ltxa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                     ctypes.c_float, vp]
+        L.ltxa_sp_pack_rope.restype = ctypes.c_int
+        L.ltxa_sp_pack_rope.argtypes = [vp, vp, vp, i64, i32, dp, i64, i32, i32, i32,
+                                        ctypes.c_double, vp]
+        L.ltxa_attn_fwd_unpack.restype = ctypes.c_int
+        L.ltxa_attn_fwd_unpack.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
+                                           ctypes.c_float, i32, vp]
         _lib = L
     return _lib
 
@@ -198,6 +204,69 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Option
     return out
 
 
+def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
+                 theta: float = 10000.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` (``ltxa_sp_pack_rope``).
+
+    Equal, bit for bit, to :func:`sp_pack` followed by :func:`rope_qk` on the
+    packed tensor.  ``pos`` is an int32 ``[N, A]`` GPU tensor.
+    """
+    _gpu(src, "src", torch.bfloat16)
+    _gpu(pos, "pos", torch.int32)
+    B, N, H, D = src.shape
+    P = int(world_size)
+    if pos.dim() != 2 or pos.shape[0] != N or pos.shape[1] != len(max_pos):
+        raise ValueError("pos must be [N, A] with one max_pos per axis")
+    if out is None:
+        if P < 1 or H % P:
+            _check("ltxa_sp_pack_rope", LTXA_E_DIVISIBILITY if P >= 1 else LTXA_E_SHAPE)
+        out = torch.empty((P, B, N, H // P, D), dtype=src.dtype, device=src.device)
+    _gpu(out, "out", torch.bfloat16)
+    if out.numel() != src.numel():
+        raise ValueError("out has the wrong number of elements")
+    _check("ltxa_sp_pack_rope", lib().ltxa_sp_pack_rope(
+        src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
+        B, H, D, P, float(theta), _stream_ptr(src)))
+    return out
+
+
+def attn_fwd_unpack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Optional[int] = None,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention over head shards ``[P, B, N, H/P, D]`` with the output in token
+    order ``[B, Nq, H, D]`` (``ltxa_attn_fwd_unpack``).
+
+    Equal, bit for bit, to :func:`attn_fwd` over the ``P * B`` shard entries
+    followed by :func:`sp_unpack`.  ``lse``, if given, is float32
+    ``[P, B, H/P, Nq]``.
+    """
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _gpu(t, name, torch.bfloat16)
+    if q.dim() != 5:
+        raise ValueError("q must be [P, B, Nq, H/P, D]")
+    P, B, Nq, Hl, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (P, B, Nk, Hl, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [P, B, Nk, H/P, D] matching q")
+    nk_valid = Nk if nk_valid is None else int(nk_valid)
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Nq, P * Hl, D), dtype=q.dtype, device=q.device)
+    _gpu(out, "out", torch.bfloat16)
+    if out.shape != (B, Nq, P * Hl, D):
+        raise ValueError("out must be [B, Nq, H, D]")
+    lse_ptr = None
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+        if lse.shape != (P, B, Hl, Nq):
+            raise ValueError("lse must be [P, B, H/P, Nq]")
+        lse_ptr = lse.data_ptr()
+    _check("ltxa_attn_fwd_unpack", lib().ltxa_attn_fwd_unpack(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, P * Hl, D, Nq, Nk,
+        nk_valid, scale, P, _stream_ptr(q)))
+    return out
+
+
 class SpShare:
     """Bookkeeping of one SP attention group held as ``world_size`` virtual
     ranks on one GPU (an ``AttentionManager`` analogue)."""
@@ -235,7 +304,7 @@ class SpShare:
 def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpShare",
                  q_pos: torch.Tensor, q_max_pos, k_pos: Optional[torch.Tensor] = None,
                  k_max_pos=None, nk_valid: Optional[int] = None, theta: float = 10000.0,
-                 scale: Optional[float] = None) -> torch.Tensor:
+                 scale: Optional[float] = None, fused: bool = True) -> torch.Tensor:
     """One layer's SP attention for every virtual rank of ``share`` on one GPU.
 
     ``q``: token-major bf16 ``[B, N_pad, H, D]`` padded to ``share.n_pad``
@@ -245,6 +314,11 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     over every valid key (``ltxa_attn_fwd``), shuffle back
     (``ltxa_sp_unpack``) and drop padded rows (a view).  Returns
     ``[B, share.n_valid, H, D]``.
+
+    With ``fused`` (the default) the same steps take four launches: Q and K
+    are exchanged and rotated in one pass each (``ltxa_sp_pack_rope``), V is
+    exchanged, and attention writes token order directly
+    (``ltxa_attn_fwd_unpack``); the result is bit-identical.
     """
     P = share.world_size
     B, N, H, D = q.shape
@@ -255,6 +329,12 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     k_max_pos = q_max_pos if k_max_pos is None else k_max_pos
     nk_valid = share.n_valid if nk_valid is None else nk_valid
     Hl = H // P
+    if fused:
+        qs = sp_pack_rope(q, q_pos, q_max_pos, P, theta)
+        ks = sp_pack_rope(k, k_pos, k_max_pos, P, theta)
+        vs = sp_pack(v, P)
+        out = attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale)
+        return out[:, :share.n_valid]
     qs = sp_pack(q, P).view(P * B, N, Hl, D)
     ks = sp_pack(k, P).view(P * B, Nk, Hl, D)
     vs = sp_pack(v, P).view(P * B, Nk, Hl, D)
