@@ -27,7 +27,9 @@ Parity status:
 * ``rope``  -- pinned by closed forms and invariants.  The frequency schedule
   itself is a reading (the page prints the function signatures only), so its
   agreement with upstream LTX-2 numerics is *parity unpinned*; the schedule
-  used here is pinned to its own closed form.
+  used here is pinned to its own closed form.  The variants (split pairing,
+  grid over the inner dimension, middle indices) are readings too, pinned to
+  hand-derived angles and to identities that reduce each to the base case.
 * ``attn``  -- pinned by brute force, closed forms and invariants.
 """
 

@@ -1,4 +1,4 @@
-"""Oracle for the interleaved rotary position embedding on Q and K.
+"""Oracle for the rotary position embedding on Q and K.
 Test infrastructure only.
 
 Source: FastVideo API page ``fastvideo.models.encoders.gemma``:
@@ -21,16 +21,36 @@ The page prints signatures only, so the following readings are taken
   ``y1 = x0 sin + x1 cos``.
 * Every head uses the same angles (the grid spans one head's channels).
 * Arithmetic in float64 throughout, no intermediate rounding.
+
+Variants (same page; ``precompute_ltx_freqs_cis`` takes ``dim``,
+``num_attention_heads``, ``use_middle_indices_grid`` and ``rope_type``, and the
+connector passes ``dim = inner_dim = heads * head_dim``; a float64 grid
+generator exists beside the float32 one):
+
+* SPLIT pairing (``LTXRopeType``'s second variant).  Reading: pair ``i`` is
+  channels ``(i, i + D/2)`` of the head (first half, second half) instead of
+  ``(2i, 2i+1)``; the rotation of a pair is unchanged.
+* Grid over the inner dimension.  Reading: the schedule above is laid over
+  ``G * D`` channels (``G * D / 2`` pairs, ``n_ax = floor((G*D/2)/A)``) and
+  head ``h`` of the ``G`` takes global pairs ``[h*D/2, (h+1)*D/2)``, so heads
+  turn at different frequencies.  ``G = 1`` is the per-head grid.
+* Middle indices.  Reading: integer positions index unit cells and the angle
+  uses the cell's middle, ``pos + 1/2``.
+* Float64 grid.  A precision choice only: the oracle is float64 throughout,
+  so it has no separate function.
 """
 
 import numpy as np
 
 
-def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float) -> np.ndarray:
+def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float, *, grid_heads: int = 1,
+                head: int = 0, middle: bool = False) -> np.ndarray:
     """Angles ``phi[n, i]`` (float64) for integer positions ``pos[n, a]``.
 
     ``pos`` has shape ``[N, A]``; ``max_pos`` has ``A`` positive entries.
-    Returns ``[N, head_dim // 2]``.
+    The schedule spans ``grid_heads * head_dim`` channels and the angles of
+    head ``head`` are returned (``grid_heads = 1``: the per-head grid).
+    ``middle`` uses ``pos + 1/2``.  Returns ``[N, head_dim // 2]``.
     """
     pos = np.asarray(pos)
     if pos.ndim != 2:
@@ -41,32 +61,54 @@ def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float) -> np.nda
         raise ValueError("max_pos needs one positive entry per axis")
     if head_dim % 2 != 0:
         raise ValueError("head_dim must be even")
-    n_pairs = head_dim // 2
+    if grid_heads < 1 or not 0 <= head < grid_heads:
+        raise ValueError("head must lie in [0, grid_heads)")
+    n_pairs = grid_heads * head_dim // 2
     n_ax = n_pairs // A
     if n_ax < 1:
         raise ValueError("fewer channel pairs than axes")
     phi = np.zeros((N, n_pairs), dtype=np.float64)
     for a in range(A):
-        frac = pos[:, a].astype(np.float64) / max_pos[a]
+        p = pos[:, a].astype(np.float64) + (0.5 if middle else 0.0)
+        frac = p / max_pos[a]
         for k in range(n_ax):
             phi[:, a * n_ax + k] = frac * (float(theta) ** (-k / n_ax))
-    return phi
+    hp = head_dim // 2
+    return phi[:, head * hp:(head + 1) * hp]
 
 
-def rope_apply(x: np.ndarray, pos: np.ndarray, max_pos, theta: float) -> np.ndarray:
+def rope_apply(x: np.ndarray, pos: np.ndarray, max_pos, theta: float, *,
+               rope_type: str = "interleaved", grid_heads: int = 0, head_offset: int = 0,
+               middle: bool = False) -> np.ndarray:
     """Rotate ``x[B, N, H, D]`` (float64) by the angles of ``pos[N, A]``.
 
-    Returns a new float64 array.  Channels (2i, 2i+1) form pair ``i``.
+    Returns a new float64 array.  ``rope_type`` "interleaved": channels
+    (2i, 2i+1) form pair ``i``; "split": channels (i, i + D/2) do.
+    ``grid_heads = 0``: every head uses the per-head grid; ``grid_heads = G``:
+    head ``j`` of ``x`` is head ``head_offset + j`` of a grid over ``G`` heads.
     """
     B, N, H, D = x.shape
     if pos.shape[0] != N:
         raise ValueError("one position row per token is required")
-    phi = rope_angles(pos, max_pos, D, theta)          # [N, D/2]
-    c = np.cos(phi)[None, :, None, :]
-    s = np.sin(phi)[None, :, None, :]
-    x0 = x[..., 0::2]
-    x1 = x[..., 1::2]
+    if rope_type not in ("interleaved", "split"):
+        raise ValueError("rope_type must be 'interleaved' or 'split'")
+    if grid_heads == 0:
+        phi = rope_angles(pos, max_pos, D, theta, middle=middle)            # [N, D/2]
+        phi = np.broadcast_to(phi[:, None, :], (N, H, D // 2))
+    else:
+        if head_offset < 0 or head_offset + H > grid_heads:
+            raise ValueError("the tensor's heads must lie inside the grid's heads")
+        phi = np.stack([rope_angles(pos, max_pos, D, theta, grid_heads=grid_heads,
+                                    head=head_offset + j, middle=middle) for j in range(H)], axis=1)
+    c = np.cos(phi)[None]                                                   # [1, N, H, D/2]
+    s = np.sin(phi)[None]
+    if rope_type == "interleaved":
+        i0, i1 = slice(0, D, 2), slice(1, D, 2)
+    else:
+        i0, i1 = slice(0, D // 2), slice(D // 2, D)
+    x0 = x[..., i0]
+    x1 = x[..., i1]
     y = np.empty_like(x, dtype=np.float64)
-    y[..., 0::2] = x0 * c - x1 * s
-    y[..., 1::2] = x0 * s + x1 * c
+    y[..., i0] = x0 * c - x1 * s
+    y[..., i1] = x0 * s + x1 * c
     return y
