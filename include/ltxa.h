@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 101 /* major*100 + minor */
+#define LTXA_VERSION 102 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -193,6 +193,62 @@ int ltxa_attn_fwd_unpack(const void* q, const void* k, const void* v, void* o, f
                          int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
                          int64_t nk_pad, int64_t nk_valid, float scale, int32_t world_size,
                          void* stream);
+
+/*
+ * Rotary variants (FastVideo gemma page: LTXRopeType's two pairings;
+ * precompute_ltx_freqs_cis's grid width `dim` with `num_attention_heads`,
+ * its `use_middle_indices_grid`, and the float64 grid generator that
+ * double_precision_rope selects).
+ */
+#define LTXA_ROPE_INTERLEAVED 0 /* pairs (2i, 2i+1) */
+#define LTXA_ROPE_SPLIT 1       /* pairs (i, i + head_dim/2) */
+
+typedef struct ltxa_rope_opts {
+  int32_t rope_type;   /* LTXA_ROPE_INTERLEAVED or LTXA_ROPE_SPLIT */
+  int32_t grid_heads;  /* 0: one grid over head_dim shared by every head.
+                          G >= 1: one grid over G * head_dim channels
+                          (G * head_dim / 2 pairs, n_ax = floor(that / axes)
+                          per axis); grid head g turns its pairs by the
+                          global pairs [g*head_dim/2, (g+1)*head_dim/2) */
+  int32_t head_offset; /* with grid_heads > 0: grid head of the tensor's head 0 */
+  int32_t fp64_angles; /* 0: angle and sin/cos in fp32; 1: in fp64 (the
+                          rotation itself stays fp32) */
+  int32_t middle;      /* 0: angle uses pos; 1: pos + 1/2 (cell middles) */
+  int32_t reserved;    /* must be 0 */
+} ltxa_rope_opts;
+
+/*
+ * ltxa_rope_ex -- rotary embedding of one bf16 tensor in place with the
+ * variants above (opts NULL = all zero = the rotation of ltxa_rope_qk,
+ * bit for bit).
+ *
+ *   x: bf16 [batch, n_tokens, heads, head_dim], rotated in place.
+ *   pos: DEVICE int32 [n_tokens, axes]; max_pos: HOST array of `axes`
+ *     values; theta: frequency base.
+ *   With grid_heads = G > 0, head j of x is grid head head_offset + j, so
+ *   head_offset + heads <= G.  A buffer of several ranks' head shards is
+ *   rotated one rank at a time (head_offset = rank * heads per rank), or
+ *   through ltxa_sp_pack_rope_ex.
+ * Errors: as ltxa_rope_qk for one tensor, plus E_NULL (pos or max_pos NULL),
+ * E_SHAPE (rope_type, fp64_angles or middle not 0/1, reserved != 0,
+ * grid_heads < 0, head_offset < 0 or head_offset + heads > grid_heads, or
+ * fewer grid pairs than axes), E_ALIGN (SPLIT with head_dim % 16 != 0).
+ */
+int ltxa_rope_ex(void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                 const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim,
+                 double theta, const ltxa_rope_opts* opts, void* stream);
+
+/*
+ * ltxa_sp_pack_rope_ex -- ltxa_sp_pack_rope with the variants above: the
+ * source head h (of `heads`) is grid head head_offset + h.  dst equals, bit
+ * for bit, ltxa_sp_pack followed by ltxa_rope_ex on each rank's shard with
+ * that rank's head offset.  Errors: those of ltxa_sp_pack_rope and
+ * ltxa_rope_ex.
+ */
+int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
+                         int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                         int32_t head_dim, int32_t world_size, double theta,
+                         const ltxa_rope_opts* opts, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

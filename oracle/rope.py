@@ -43,15 +43,10 @@ generator exists beside the float32 one):
 import numpy as np
 
 
-def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float, *, grid_heads: int = 1,
-                head: int = 0, middle: bool = False) -> np.ndarray:
-    """Angles ``phi[n, i]`` (float64) for integer positions ``pos[n, a]``.
-
-    ``pos`` has shape ``[N, A]``; ``max_pos`` has ``A`` positive entries.
-    The schedule spans ``grid_heads * head_dim`` channels and the angles of
-    head ``head`` are returned (``grid_heads = 1``: the per-head grid).
-    ``middle`` uses ``pos + 1/2``.  Returns ``[N, head_dim // 2]``.
-    """
+def _schedule(pos: np.ndarray, max_pos, n_pairs: int, theta: float, middle: bool) -> np.ndarray:
+    """Angles of all ``n_pairs`` pairs of one grid: ``n_ax = floor(n_pairs/A)``
+    pairs per axis in axis order; pair ``a*n_ax + k`` turns by
+    ``(pos[a] (+ 1/2) / max_pos[a]) * theta**(-k/n_ax)``; the rest stay at 0."""
     pos = np.asarray(pos)
     if pos.ndim != 2:
         raise ValueError("pos must be [N, A]")
@@ -59,11 +54,6 @@ def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float, *, grid_h
     max_pos = [float(m) for m in max_pos]
     if len(max_pos) != A or any(m <= 0 for m in max_pos):
         raise ValueError("max_pos needs one positive entry per axis")
-    if head_dim % 2 != 0:
-        raise ValueError("head_dim must be even")
-    if grid_heads < 1 or not 0 <= head < grid_heads:
-        raise ValueError("head must lie in [0, grid_heads)")
-    n_pairs = grid_heads * head_dim // 2
     n_ax = n_pairs // A
     if n_ax < 1:
         raise ValueError("fewer channel pairs than axes")
@@ -73,7 +63,24 @@ def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float, *, grid_h
         frac = p / max_pos[a]
         for k in range(n_ax):
             phi[:, a * n_ax + k] = frac * (float(theta) ** (-k / n_ax))
+    return phi
+
+
+def rope_angles(pos: np.ndarray, max_pos, head_dim: int, theta: float, *, grid_heads: int = 1,
+                head: int = 0, middle: bool = False) -> np.ndarray:
+    """Angles ``phi[n, i]`` (float64) for integer positions ``pos[n, a]``.
+
+    ``pos`` has shape ``[N, A]``; ``max_pos`` has ``A`` positive entries.
+    The schedule spans ``grid_heads * head_dim`` channels and the angles of
+    head ``head`` are returned (``grid_heads = 1``: the per-head grid).
+    ``middle`` uses ``pos + 1/2``.  Returns ``[N, head_dim // 2]``.
+    """
+    if head_dim % 2 != 0:
+        raise ValueError("head_dim must be even")
+    if grid_heads < 1 or not 0 <= head < grid_heads:
+        raise ValueError("head must lie in [0, grid_heads)")
     hp = head_dim // 2
+    phi = _schedule(pos, max_pos, grid_heads * hp, theta, middle)
     return phi[:, head * hp:(head + 1) * hp]
 
 
@@ -98,8 +105,11 @@ def rope_apply(x: np.ndarray, pos: np.ndarray, max_pos, theta: float, *,
     else:
         if head_offset < 0 or head_offset + H > grid_heads:
             raise ValueError("the tensor's heads must lie inside the grid's heads")
-        phi = np.stack([rope_angles(pos, max_pos, D, theta, grid_heads=grid_heads,
-                                    head=head_offset + j, middle=middle) for j in range(H)], axis=1)
+        if D % 2 != 0:
+            raise ValueError("head_dim must be even")
+        hp = D // 2
+        wide = _schedule(pos, max_pos, grid_heads * hp, theta, middle)     # [N, G*D/2]
+        phi = wide.reshape(N, grid_heads, hp)[:, head_offset:head_offset + H]
     c = np.cos(phi)[None]                                                   # [1, N, H, D/2]
     s = np.sin(phi)[None]
     if rope_type == "interleaved":

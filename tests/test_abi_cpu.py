@@ -162,6 +162,48 @@ def test_attn_unpack_errors(L):
     assert f(A, B, C, D_, None, 1 << 40, 1 << 13, 128, 232, 232, 231, 0.1, 1 << 13, None) == ltxa.LTXA_E_RANGE
 
 
+def _opts(**kw):
+    return ctypes.byref(ltxa.rope_opts(**kw)) if kw else None
+
+
+def _raw_opts(*vals):
+    return ctypes.byref(ltxa.RopeOpts(*vals))
+
+
+def test_rope_ex_errors(L):
+    f = L.ltxa_rope_ex
+    mp3 = _mp(3, 7, 11)
+    # x, pos, n, axes, max_pos, batch, heads, head_dim, theta, opts
+    assert f(None, C, 232, 3, mp3, 1, 4, 64, 1e4, None, None) == ltxa.LTXA_E_NULL
+    assert f(A, None, 232, 3, mp3, 1, 4, 64, 1e4, None, None) == ltxa.LTXA_E_NULL
+    assert f(A, C, 232, 3, None, 1, 4, 64, 1e4, None, None) == ltxa.LTXA_E_NULL
+    assert f(A, C, 232, 3, mp3, 0, 4, 64, 1e4, None, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, C, 232, 3, mp3, 1, 4, 62, 1e4, None, None) == ltxa.LTXA_E_ALIGN
+    assert f(A + 2, C, 232, 3, mp3, 1, 4, 64, 1e4, None, None) == ltxa.LTXA_E_ALIGN
+    bad = [(2, 0, 0, 0, 0, 0), (0, 0, 0, 2, 0, 0), (0, 0, 0, 0, 2, 0), (0, 0, 0, 0, 0, 1),
+           (0, -1, 0, 0, 0, 0), (0, 4, -1, 0, 0, 0), (0, 4, 1, 0, 0, 0), (0, 3, 0, 0, 0, 0)]
+    for vals in bad:
+        assert f(A, C, 232, 3, mp3, 1, 4, 64, 1e4, _raw_opts(*vals), None) == ltxa.LTXA_E_SHAPE, vals
+    # Fewer grid pairs than axes: one head of 4 channels has 2 pairs.
+    assert f(A, C, 232, 3, mp3, 1, 1, 4, 1e4, _opts(grid_heads=1), None) in (ltxa.LTXA_E_SHAPE,
+                                                                            ltxa.LTXA_E_ALIGN)
+    # SPLIT needs 16-element halves-of-8: head_dim % 16 == 0.
+    assert f(A, C, 232, 3, mp3, 1, 4, 24, 1e4, _opts(rope_type="split"), None) == ltxa.LTXA_E_ALIGN
+
+
+def test_pack_rope_ex_errors(L):
+    f = L.ltxa_sp_pack_rope_ex
+    mp3 = _mp(3, 7, 11)
+    args = (232, 3, mp3, 1, 4, 64, 2, 1e4)
+    assert f(None, B, C, *args, None, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, 231, 3, mp3, 1, 4, 64, 2, 1e4, None, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, A + 256, C, *args, None, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, *args, _opts(grid_heads=3), None) == ltxa.LTXA_E_SHAPE     # 4 heads > 3
+    assert f(A, B, C, *args, _opts(grid_heads=5, head_offset=2), None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, *args, _raw_opts(0, 0, 0, 0, 0, 7), None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 3, mp3, 1, 4, 40, 2, 1e4, _opts(rope_type="split"), None) == ltxa.LTXA_E_ALIGN
+
+
 def test_sp_share_bookkeeping():
     s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096

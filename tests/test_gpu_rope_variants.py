@@ -1,0 +1,141 @@
+"""GPU parity of the rotary variants (``ltxa_rope_ex``, ``ltxa_sp_pack_rope_ex``)
+against the fp64 oracle.
+
+Source: FastVideo gemma page -- ``LTXRopeType`` (interleaved and split
+pairings), ``precompute_ltx_freqs_cis`` (grid width ``dim`` with
+``num_attention_heads``, ``use_middle_indices_grid``), the float64 grid
+generator selected by ``double_precision_rope``, and the 1D connector, which
+passes the inner dimension.  Bar: the rotary bar of the base case (within
+one bf16 ulp of the exact rotation, or within 2^-20 (|x0| + |x1|) where the
+result cancels), and more than 99.5 % of outputs equal to the exact result
+rounded to bf16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import bits, f64, rope_ok
+from video_dit_sequence_amd import ltxa
+from video_dit_sequence_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+VARIANTS = [
+    dict(rope_type="interleaved"),
+    dict(rope_type="split"),
+    dict(rope_type="interleaved", middle=True),
+    dict(rope_type="interleaved", fp64_angles=True),
+    dict(rope_type="split", fp64_angles=True, middle=True),
+    dict(rope_type="interleaved", grid_heads=-1),              # -1: grid over the tensor's heads
+    dict(rope_type="split", grid_heads=-1, fp64_angles=True),
+    dict(rope_type="interleaved", grid_heads=-2, head_offset=3),  # -2: twice the heads, offset 3
+]
+
+
+def _opts(v, heads):
+    v = dict(v)
+    g = v.get("grid_heads", 0)
+    if g < 0:
+        v["grid_heads"] = -g * heads
+    return v
+
+
+def _oracle_kw(v):
+    return dict(rope_type=v.get("rope_type", "interleaved"), grid_heads=v.get("grid_heads", 0),
+                head_offset=v.get("head_offset", 0), middle=v.get("middle", False))
+
+
+def _name(v):
+    return "-".join(f"{k}={val}" for k, val in v.items())
+
+
+@pytest.mark.parametrize("name,heads", [("tiny_231", 4), ("full_6144", 32), ("connector_1024", 32)])
+@pytest.mark.parametrize("variant", VARIANTS, ids=_name)
+def test_rope_variant_matches_oracle(name, heads, variant):
+    w = wl.WORKLOADS[name]
+    v = _opts(variant, heads)
+    print(f"rope_ex {name} H={heads} {v}", flush=True)
+    q, _, _ = wl.qkv(w, heads=heads)
+    qpos, _ = wl.positions(w)
+    xg = q.to(DEV)
+    ltxa.rope(xg, torch.from_numpy(qpos).to(DEV), w.q_max_pos, w.theta, opts=ltxa.rope_opts(**v))
+    torch.cuda.synchronize()
+    # Rotation acts token by token: the oracle checks every token of small
+    # cases and a head/tail/strided token sample of large ones.
+    N = q.shape[1]
+    sel = np.arange(N) if N <= 1024 else np.unique(np.r_[0:256, N - 256:N, 256:N - 256:37])
+    x = f64(q)[:, sel]
+    ref = oracle.rope_apply(x, qpos[sel], w.q_max_pos, w.theta, **_oracle_kw(v))
+    got = f64(xg)[:, sel]
+    if v.get("rope_type") == "split":
+        D = x.shape[-1]
+        # rope_ok pairs channels (2i, 2i+1): give it the pair partners side by side.
+        perm = np.empty(D, dtype=np.int64)
+        perm[0::2], perm[1::2] = np.arange(D // 2), np.arange(D // 2, D)
+        got, ref, x = got[..., perm], ref[..., perm], x[..., perm]
+    ok, exact = rope_ok(got, ref, x)
+    assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
+    assert exact > 0.995, exact
+
+
+def test_default_options_are_rope_qk_bit_exact():
+    w = wl.WORKLOADS["full_6144"]
+    q, _, _ = wl.qkv(w)
+    qpos, _ = wl.positions(w)
+    pg = torch.from_numpy(qpos).to(DEV)
+    a, b, c = q.to(DEV), q.to(DEV), q.to(DEV)
+    ltxa.rope_qk(a, pg, w.q_max_pos, None, None, None, w.theta)
+    ltxa.rope(b, pg, w.q_max_pos, w.theta)                          # opts NULL
+    ltxa.rope(c, pg, w.q_max_pos, w.theta, opts=ltxa.rope_opts())   # all-zero options
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(a), bits(c))
+
+
+@pytest.mark.parametrize("variant", [dict(rope_type="split"), dict(grid_heads=-1),
+                                     dict(rope_type="split", grid_heads=-1, fp64_angles=True, middle=True)],
+                         ids=_name)
+def test_pack_rope_ex_equals_pack_then_per_rank_rope(variant):
+    w = wl.WORKLOADS["share_32768"]
+    P, H = 8, 32
+    v = _opts(variant, H)
+    print(f"pack_rope_ex share_32768 {v}", flush=True)
+    g = torch.Generator().manual_seed(91)
+    x = wl.randn_bf16((1, 4096, H, 128), g).to(DEV)
+    pos = torch.from_numpy(wl.video_positions((2, 32, 64))).to(DEV)
+    fused = ltxa.sp_pack_rope(x, pos, (2, 32, 64), P, w.theta, opts=ltxa.rope_opts(**v))
+    two = ltxa.sp_pack(x, P)
+    for p in range(P):
+        vp = dict(v)
+        if vp.get("grid_heads", 0):
+            vp["head_offset"] = vp.get("head_offset", 0) + p * (H // P)
+        ltxa.rope(two[p], pos, (2, 32, 64), w.theta, opts=ltxa.rope_opts(**vp))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(fused), bits(two))
+
+
+def test_fp64_angles_hold_the_bar_at_large_angles():
+    # Unnormalised positions (max_pos 1) turn by up to ~32767 rad, where an
+    # fp32 angle is off by ~1e-3 rad; the fp64 angle path stays within the bar.
+    g = torch.Generator().manual_seed(92)
+    N, H, D = 32768, 2, 64
+    x = wl.randn_bf16((1, N, H, D), g)
+    pos = wl.audio_positions(N)
+    xg = x.to(DEV)
+    ltxa.rope(xg, torch.from_numpy(pos).to(DEV), (1.0,), 10000.0, opts=ltxa.rope_opts(fp64_angles=True))
+    torch.cuda.synchronize()
+    ref = oracle.rope_apply(f64(x), pos, (1.0,), 10000.0)
+    ok, exact = rope_ok(f64(xg), ref, f64(x))
+    assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
+    assert exact > 0.995, exact
+
+
+def test_variant_options_rejected():
+    x = torch.zeros((1, 8, 4, 64), dtype=torch.bfloat16, device=DEV)
+    pos = torch.zeros((8, 3), dtype=torch.int32, device=DEV)
+    with pytest.raises(ltxa.LtxaError):
+        ltxa.rope(x, pos, (1, 1, 1), opts=ltxa.rope_opts(grid_heads=2))        # 4 heads > grid of 2
+    with pytest.raises(ltxa.LtxaError):
+        ltxa.rope(x[..., :8].contiguous(), pos, (1, 1, 1), opts=ltxa.rope_opts(rope_type="split"))

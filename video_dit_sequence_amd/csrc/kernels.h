@@ -9,23 +9,41 @@
 
 namespace ltxa {
 
-// Per-pair rotary table built on the host: pair i turns by pos[axis[i]] * coef[i];
-// axis[i] < 0 marks a pair that is left as it is.
+// Per-pair rotary table of the head-shared grid, built on the host in fp64:
+// pair i turns by (pos[axis[i]] + mid) * coef[i]; axis[i] < 0 marks a pair
+// that is left as it is.  The fp32 path rounds coef[i] to fp32.
 struct RopeTable {
-  float coef[128];
+  double coef[128];
   int32_t axis[128];
+};
+
+// Grid over the inner dimension of grid_heads heads: global pair gp turns by
+// (pos[gp / n_ax] + mid) * theta^(-(gp % n_ax) / n_ax) / max_pos[gp / n_ax]
+// while gp / n_ax < axes; the tensor's head h is grid head head_offset + h.
+struct RopeInner {
+  double theta;
+  double max_pos[3];
+  int32_t n_ax;
+  int32_t head_offset;
+};
+
+struct RopeMode {
+  bool split;   // pairs (i, i + head_dim/2) instead of (2i, 2i+1)
+  bool inner;   // RopeInner grid instead of the shared RopeTable
+  bool f64;     // angles and sin/cos in fp64
+  double mid;   // 0, or 0.5 for cell-middle positions
 };
 
 hipError_t launch_perm(const void* src, void* dst, const PermPlan& plan, int world_size,
                        bool to_packed, hipStream_t stream);
 
-hipError_t launch_rope(uint16_t* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
-                       int64_t batch, int32_t heads, int32_t head_dim, const RopeTable& table,
-                       hipStream_t stream);
-
-hipError_t launch_pack_rope(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
-                            int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                            const RopeTable& table, hipStream_t stream);
+// Rotary embedding of src [batch, n_tokens, heads, head_dim] into dst
+// [ranks, batch, n_tokens, heads/ranks, head_dim]; ranks = 1 with dst = src
+// rotates in place.
+hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
+                           int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
+                           const RopeMode& mode, const RopeTable& table, const RopeInner& inner,
+                           hipStream_t stream);
 
 // Attention over [batch, nq, heads, head_dim] operands.  The output row of
 // (batch entry bb, token n, head h) is written at head slot

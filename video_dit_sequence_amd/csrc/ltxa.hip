@@ -13,7 +13,7 @@ namespace {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LTXA_OK : LTXA_E_HIP; }
 
-// Frequencies of the interleaved rotary schedule, in fp64 on the host: with
+// Frequencies of the head-shared rotary schedule, in fp64 on the host: with
 // A axes and head_dim/2 pairs, axis a owns pairs [a*n_ax, (a+1)*n_ax), and
 // pair a*n_ax + j turns by pos[a] * theta^(-j/n_ax) / max_pos[a]; the
 // leftover highest pairs stay unrotated.
@@ -22,16 +22,49 @@ ltxa::RopeTable rope_table(int32_t head_dim, int32_t axes, const double* max_pos
   const int pairs = head_dim / 2;
   const int per_axis = pairs / axes;
   for (int i = 0; i < 128; ++i) {
-    t.coef[i] = 0.0f;
+    t.coef[i] = 0.0;
     t.axis[i] = -1;
   }
   for (int a = 0; a < axes; ++a)
     for (int j = 0; j < per_axis; ++j) {
       const int i = a * per_axis + j;
-      t.coef[i] = static_cast<float>(std::pow(theta, -static_cast<double>(j) / per_axis) / max_pos[a]);
+      t.coef[i] = std::pow(theta, -static_cast<double>(j) / per_axis) / max_pos[a];
       t.axis[i] = a;
     }
   return t;
+}
+
+// The same schedule laid over grid_heads * head_dim channels.
+ltxa::RopeInner rope_inner(const ltxa_rope_opts* opts, int32_t head_dim, int32_t axes, const double* max_pos,
+                           double theta) {
+  ltxa::RopeInner g{};
+  g.theta = theta;
+  for (int a = 0; a < 3; ++a) g.max_pos[a] = a < axes ? max_pos[a] : 1.0;
+  if (opts && opts->grid_heads > 0) {
+    g.n_ax = static_cast<int32_t>(int64_t(opts->grid_heads) * (head_dim / 2) / axes);
+    g.head_offset = opts->head_offset;
+  }
+  return g;
+}
+
+ltxa::RopeMode rope_mode(const ltxa_rope_opts* opts) {
+  ltxa::RopeMode m{false, false, false, 0.0};
+  if (opts) {
+    m.split = opts->rope_type == LTXA_ROPE_SPLIT;
+    m.inner = opts->grid_heads > 0;
+    m.f64 = opts->fp64_angles != 0;
+    m.mid = opts->middle ? 0.5 : 0.0;
+  }
+  return m;
+}
+
+int rope_launch(const void* src, void* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
+                double theta, const ltxa_rope_opts* opts, void* stream) {
+  return launch_status(ltxa::launch_rope_any(
+      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), pos, n_tokens, axes, batch, heads,
+      head_dim, ranks, rope_mode(opts), rope_table(head_dim, axes, max_pos, theta),
+      rope_inner(opts, head_dim, axes, max_pos, theta), static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -81,16 +114,12 @@ LTXA_EXPORT int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t 
   const int rc = ltxa::check_rope(q, q_pos, nq, q_axes, q_max_pos, k, k_pos, nk, k_axes, k_max_pos,
                                   batch, heads, head_dim, theta);
   if (rc) return rc;
-  auto s = static_cast<hipStream_t>(stream);
   if (q) {
-    const int r = launch_status(ltxa::launch_rope(static_cast<uint16_t*>(q), q_pos, nq, q_axes, batch,
-                                                  heads, head_dim,
-                                                  rope_table(head_dim, q_axes, q_max_pos, theta), s));
+    const int r = rope_launch(q, q, q_pos, nq, q_axes, q_max_pos, batch, heads, head_dim, 1, theta, nullptr,
+                              stream);
     if (r) return r;
   }
-  if (k)
-    return launch_status(ltxa::launch_rope(static_cast<uint16_t*>(k), k_pos, nk, k_axes, batch, heads,
-                                           head_dim, rope_table(head_dim, k_axes, k_max_pos, theta), s));
+  if (k) return rope_launch(k, k, k_pos, nk, k_axes, k_max_pos, batch, heads, head_dim, 1, theta, nullptr, stream);
   return LTXA_OK;
 }
 
@@ -109,10 +138,29 @@ LTXA_EXPORT int ltxa_sp_pack_rope(const void* src, void* dst, const int32_t* pos
   const int rc = ltxa::check_pack_rope(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim,
                                        world_size, theta);
   if (rc) return rc;
-  return launch_status(ltxa::launch_pack_rope(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
-                                              pos, n_tokens, axes, batch, heads, head_dim, world_size,
-                                              rope_table(head_dim, axes, max_pos, theta),
-                                              static_cast<hipStream_t>(stream)));
+  return rope_launch(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim, world_size, theta, nullptr,
+                     stream);
+}
+
+LTXA_EXPORT int ltxa_rope_ex(void* x, const int32_t* pos, int64_t n_tokens, int32_t axes, const double* max_pos,
+                             int64_t batch, int32_t heads, int32_t head_dim, double theta,
+                             const ltxa_rope_opts* opts, void* stream) {
+  const int rc = ltxa::check_rope_ex(x, pos, n_tokens, axes, max_pos, batch, heads, head_dim, theta, opts);
+  if (rc) return rc;
+  return rope_launch(x, x, pos, n_tokens, axes, max_pos, batch, heads, head_dim, 1, theta, opts, stream);
+}
+
+LTXA_EXPORT int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
+                                     int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                                     int32_t head_dim, int32_t world_size, double theta,
+                                     const ltxa_rope_opts* opts, void* stream) {
+  int rc = ltxa::check_pack_rope(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim, world_size,
+                                 theta);
+  if (rc) return rc;
+  rc = ltxa::check_rope_opts(opts, heads, head_dim, axes);
+  if (rc) return rc;
+  return rope_launch(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim, world_size, theta, opts,
+                     stream);
 }
 
 LTXA_EXPORT int ltxa_attn_fwd_unpack(const void* q, const void* k, const void* v, void* o, float* lse,

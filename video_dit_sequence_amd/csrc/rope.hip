@@ -1,22 +1,29 @@
-// Interleaved rotary embedding applied in place to a bf16 [batch, tokens,
-// heads, head_dim] tensor (FastVideo gemma page: LTXRopeType INTERLEAVED
-// rotates channel pairs (2i, 2i+1); precompute_ltx_freqs_cis turns integer
-// (t, x, y) positions, normalised by max_pos, into angles with base theta;
-// apply_ltx_rotary_emb multiplies each pair by (cos, sin)).
+// Rotary position embedding on bf16 [batch, tokens, heads, head_dim] tensors
+// (FastVideo gemma page: LTXRopeType names an INTERLEAVED pairing, channels
+// (2i, 2i+1), and a SPLIT one, channels (i, i + head_dim/2);
+// precompute_ltx_freqs_cis turns integer (t, x, y) positions, normalised by
+// max_pos, into angles with base theta, optionally at cell middles and over
+// the whole inner dimension of all heads; apply_ltx_rotary_emb multiplies
+// each pair by (cos, sin)).
 //
-// One thread owns one token and one group of 4 pairs (16 bytes of a head
-// row).  It computes the 4 angles and their cos/sin once, in fp32, and
-// applies them to that 16-byte slice of every head and batch entry, so the
-// transcendentals are amortised over batch * heads rows.  Lanes of a wave
-// cover consecutive 16-byte slices of consecutive tokens: each head row is
-// read and written in full, once, with 16-byte accesses.
+// Every kernel reads a token-major tensor and writes the rotated rows either
+// back in place (ranks = 1, dst = src) or straight into the per-rank head
+// shards [ranks, batch, tokens, heads/ranks, head_dim] that ltxa_sp_pack
+// produces, so the exchange and the rotation cost one pass over HBM.  In
+// place and packed outputs come from the same instructions, so they agree
+// bit for bit.
 //
-// Two kernels share that arithmetic: rope_kernel rotates a tensor in place;
-// pack_rope_kernel reads the token-major tensor and writes the rotated rows
-// straight into the per-rank head shards (the layout of ltxa_sp_pack), so
-// the exchange and the rotation cost one pass over HBM instead of two.  Both
-// compute every output with the same instructions, so they agree bit for
-// bit.
+// Two thread mappings, by where the angles vary:
+//  * Shared grid (every head turns by the same angles).  One thread owns one
+//    token and one group of 4 pairs (interleaved: 16 contiguous bytes) or 8
+//    pairs (split: 16 bytes in each half of the head).  It computes the
+//    cos/sin of its pairs once and applies them to every (batch, head) row
+//    of that token, so the transcendentals are amortised over batch * heads
+//    rows.  Lanes cover consecutive groups of consecutive tokens.
+//  * Inner grid (heads turn at different frequencies).  One thread owns one
+//    head and one pair group for a run of tokens: its frequencies are
+//    computed once (fp64 pow) and reused across the run; the cos/sin are
+//    per token.  Lanes cover the groups of one head row, then tokens.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,135 +32,222 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsInFlight = 4;
+constexpr int kInnerTokensPerThread = 8;
 
-__device__ __forceinline__ u32x4 rotate4(u32x4 w, const float (&c)[4], const float (&s)[4]) {
+// cos/sin of the angle (pos + mid) * coef; fp32 or fp64 evaluation.
+template <bool F64>
+__device__ __forceinline__ void turn(int32_t p, double mid, double coef, float& c, float& s) {
+  if constexpr (F64) {
+    const double phi = (static_cast<double>(p) + mid) * coef;
+    double sd, cd;
+    sincos(phi, &sd, &cd);
+    c = static_cast<float>(cd);
+    s = static_cast<float>(sd);
+  } else {
+    const float phi = (static_cast<float>(p) + static_cast<float>(mid)) * static_cast<float>(coef);
+    sincosf(phi, &s, &c);
+  }
+}
+
+__device__ __forceinline__ void rot(float x0, float x1, float c, float s, float& y0, float& y1) {
+  y0 = __builtin_fmaf(x0, c, -x1 * s);
+  y1 = __builtin_fmaf(x0, s, x1 * c);
+}
+
+// Interleaved: one 16-byte word holds pairs 4g .. 4g+3 as (x0, x1) halves.
+__device__ __forceinline__ u32x4 rotate_interleaved(u32x4 w, const float* c, const float* s) {
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x0 = bf16lo_to_f32(w[i]);
-    const float x1 = bf16hi_to_f32(w[i]);
-    const float y0 = __builtin_fmaf(x0, c[i], -x1 * s[i]);
-    const float y1 = __builtin_fmaf(x0, s[i], x1 * c[i]);
+    float y0, y1;
+    rot(bf16lo_to_f32(w[i]), bf16hi_to_f32(w[i]), c[i], s[i], y0, y1);
     r[i] = pack_bf16x2(y0, y1);
   }
   return r;
 }
 
-// cos and sin of the 4 pairs 4g..4g+3 of token n: phi = pos[axis] * coef.
-__device__ __forceinline__ void pair_angles(const RopeTable& table, const int32_t* __restrict__ pos,
-                                            int64_t n, int32_t axes, int g, float (&c)[4], float (&s)[4]) {
+// Split: lo holds x0 of pairs 8g .. 8g+7, hi holds their x1.
+__device__ __forceinline__ void rotate_split(u32x4& lo, u32x4& hi, const float* c, const float* s) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pair = 4 * g + i;
-    const int a = table.axis[pair];
-    c[i] = 1.0f;
-    s[i] = 0.0f;
-    if (a >= 0) {
-      const float phi = static_cast<float>(pos[n * axes + a]) * table.coef[pair];
-      sincosf(phi, &s[i], &c[i]);
-    }
+    float a0, a1, b0, b1;
+    rot(bf16lo_to_f32(lo[i]), bf16lo_to_f32(hi[i]), c[2 * i], s[2 * i], a0, a1);
+    rot(bf16hi_to_f32(lo[i]), bf16hi_to_f32(hi[i]), c[2 * i + 1], s[2 * i + 1], b0, b1);
+    lo[i] = pack_bf16x2(a0, b0);
+    hi[i] = pack_bf16x2(a1, b1);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rope_kernel(uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ pos,
-                                                        int64_t n_tokens, int32_t axes, int64_t batch,
-                                                        int32_t heads, int32_t head_dim, RopeTable table) {
-  const int groups = head_dim >> 3;  // 8 channels = 4 pairs per thread
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t n = t / groups;
-  const int g = static_cast<int>(t - n * groups);
-  if (n >= n_tokens) return;
+// Row base pointers of (batch entry b, token n, head h): source in the
+// token-major layout, destination in the rank-sharded one (rank h / hl).
+struct RowAddr {
+  const uint16_t* src;
+  uint16_t* dst;
+};
+__device__ __forceinline__ RowAddr row_addr(const uint16_t* src, uint16_t* dst, int64_t b, int64_t n,
+                                            int64_t h, int64_t n_tokens, int32_t heads, int32_t hl,
+                                            int64_t batch, int32_t head_dim) {
+  const int64_t p = h / hl, j = h - p * hl;
+  return {src + ((b * n_tokens + n) * heads + h) * head_dim,
+          dst + (((p * batch + b) * n_tokens + n) * hl + j) * head_dim};
+}
 
-  float c[4], s[4];
-  pair_angles(table, pos, n, axes, g, c, s);
-
-  const int64_t rows = batch * heads;
-  const int64_t row_stride = head_dim;            // elements between heads of one token
-  const int64_t tok_stride = int64_t(heads) * head_dim;
-  for (int64_t r0 = 0; r0 < rows; r0 += kRowsInFlight) {
-    u32x4 w[kRowsInFlight];
-    u32x4* p[kRowsInFlight];
-#pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) {
-      const int64_t r = r0 + u;
-      p[u] = nullptr;
-      if (r < rows) {
-        const int64_t b = r / heads, h = r - b * heads;
-        uint16_t* row = x + (b * n_tokens + n) * tok_stride + h * row_stride + 8 * g;
-        p[u] = reinterpret_cast<u32x4*>(row);
-        w[u] = *p[u];
-      }
-    }
+template <bool SPLIT>
+__device__ __forceinline__ void rotate_rows(const RowAddr* a, int count, int g, int half, const float* c,
+                                            const float* s) {
+  if constexpr (SPLIT) {
+    u32x4 lo[kRowsInFlight], hi[kRowsInFlight];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u)
-      if (p[u]) *p[u] = rotate4(w[u], c, s);
+      if (u < count) {
+        lo[u] = *reinterpret_cast<const u32x4*>(a[u].src + 8 * g);
+        hi[u] = *reinterpret_cast<const u32x4*>(a[u].src + half + 8 * g);
+      }
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u)
+      if (u < count) {
+        rotate_split(lo[u], hi[u], c, s);
+        *reinterpret_cast<u32x4*>(a[u].dst + 8 * g) = lo[u];
+        *reinterpret_cast<u32x4*>(a[u].dst + half + 8 * g) = hi[u];
+      }
+  } else {
+    u32x4 w[kRowsInFlight];
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u)
+      if (u < count) w[u] = *reinterpret_cast<const u32x4*>(a[u].src + 8 * g);
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u)
+      if (u < count) *reinterpret_cast<u32x4*>(a[u].dst + 8 * g) = rotate_interleaved(w[u], c, s);
   }
 }
 
-// src: token-major [batch, n_tokens, heads, head_dim]; dst: per-rank shards
-// [ranks, batch, n_tokens, heads/ranks, head_dim].
-__global__ __launch_bounds__(kThreads) void pack_rope_kernel(const uint16_t* __restrict__ src,
-                                                             uint16_t* __restrict__ dst,
-                                                             const int32_t* __restrict__ pos,
-                                                             int64_t n_tokens, int32_t axes, int64_t batch,
-                                                             int32_t heads, int32_t head_dim, int32_t ranks,
-                                                             RopeTable table) {
-  const int groups = head_dim >> 3;
+template <bool SPLIT, bool F64>
+__global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* src, uint16_t* dst,
+                                                               const int32_t* __restrict__ pos,
+                                                               int64_t n_tokens, int32_t axes, int64_t batch,
+                                                               int32_t heads, int32_t head_dim, int32_t ranks,
+                                                               double mid, RopeTable table) {
+  constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
+  const int groups = head_dim / (2 * PPT);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t n = t / groups;
   const int g = static_cast<int>(t - n * groups);
   if (n >= n_tokens) return;
 
-  float c[4], s[4];
-  pair_angles(table, pos, n, axes, g, c, s);
+  float c[PPT], s[PPT];
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    const int pair = PPT * g + e;
+    const int a = table.axis[pair];
+    c[e] = 1.0f;
+    s[e] = 0.0f;
+    if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
+  }
 
   const int32_t hl = heads / ranks;
   const int64_t rows = batch * heads;
   for (int64_t r0 = 0; r0 < rows; r0 += kRowsInFlight) {
-    u32x4 w[kRowsInFlight];
-    u32x4* out[kRowsInFlight];
+    RowAddr a[kRowsInFlight];
+    const int count = rows - r0 < kRowsInFlight ? static_cast<int>(rows - r0) : kRowsInFlight;
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int64_t r = r0 + u;
-      out[u] = nullptr;
-      if (r < rows) {
-        const int64_t b = r / heads, h = r - b * heads;
-        const int64_t p = h / hl, j = h - p * hl;
-        w[u] = *reinterpret_cast<const u32x4*>(src + ((b * n_tokens + n) * heads + h) * head_dim + 8 * g);
-        out[u] = reinterpret_cast<u32x4*>(dst + (((p * batch + b) * n_tokens + n) * hl + j) * head_dim + 8 * g);
-      }
+      const int64_t b = r / heads, h = r - b * heads;
+      a[u] = row_addr(src, dst, b, n, h, n_tokens, heads, hl, batch, head_dim);
     }
-#pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u)
-      if (out[u]) *out[u] = rotate4(w[u], c, s);
+    rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
   }
+}
+
+template <bool SPLIT, bool F64>
+__global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* src, uint16_t* dst,
+                                                              const int32_t* __restrict__ pos,
+                                                              int64_t n_tokens, int32_t axes, int64_t batch,
+                                                              int32_t heads, int32_t head_dim, int32_t ranks,
+                                                              double mid, RopeInner grid) {
+  constexpr int PPT = SPLIT ? 8 : 4;
+  const int groups = head_dim / (2 * PPT);
+  const int lanes_per_token = groups;
+  const int token_lanes = kThreads / lanes_per_token;
+  const int g = threadIdx.x % groups;
+  const int tl = threadIdx.x / groups;
+  if (tl >= token_lanes) return;
+  const int32_t h = blockIdx.y;
+
+  // Frequencies of this thread's pairs: global pair gp of the grid's
+  // grid_heads * head_dim / 2 pairs; axis gp / n_ax, index gp % n_ax.
+  double coef[PPT];
+  int axis[PPT];
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    const int64_t gp = (static_cast<int64_t>(grid.head_offset) + h) * (head_dim / 2) + PPT * g + e;
+    const int64_t a = gp / grid.n_ax, k = gp - a * grid.n_ax;
+    axis[e] = a < axes ? static_cast<int>(a) : -1;
+    coef[e] = a < axes ? pow(grid.theta, -static_cast<double>(k) / grid.n_ax) / grid.max_pos[a < axes ? a : 0]
+                       : 0.0;
+  }
+
+  const int32_t hl = heads / ranks;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kInnerTokensPerThread * token_lanes + tl;
+  for (int i = 0; i < kInnerTokensPerThread; ++i) {
+    const int64_t n = n0 + static_cast<int64_t>(i) * token_lanes;
+    if (n >= n_tokens) break;
+    float c[PPT], s[PPT];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      c[e] = 1.0f;
+      s[e] = 0.0f;
+      if (axis[e] >= 0) turn<F64>(pos[n * axes + axis[e]], mid, coef[e], c[e], s[e]);
+    }
+    for (int64_t b0 = 0; b0 < batch; b0 += kRowsInFlight) {
+      RowAddr a[kRowsInFlight];
+      const int count = batch - b0 < kRowsInFlight ? static_cast<int>(batch - b0) : kRowsInFlight;
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u)
+        a[u] = row_addr(src, dst, b0 + u, n, h, n_tokens, heads, hl, batch, head_dim);
+      rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
+    }
+  }
+}
+
+template <bool SPLIT, bool F64>
+hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                       int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, const RopeMode& mode,
+                       const RopeTable& table, const RopeInner& inner, hipStream_t stream) {
+  constexpr int PPT = SPLIT ? 8 : 4;
+  const int groups = head_dim / (2 * PPT);
+  if (!mode.inner) {
+    const int64_t blocks = (n_tokens * groups + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                       0, stream, src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode.mid, table);
+  } else {
+    const int64_t per_block = int64_t(kInnerTokensPerThread) * (kThreads / groups);
+    const int64_t blocks = (n_tokens + per_block - 1) / per_block;
+    if (blocks > 0x7fffffff || heads > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rope_inner_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks), heads),
+                       dim3(kThreads), 0, stream, src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks,
+                       mode.mid, inner);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_pack_rope(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
-                            int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                            const RopeTable& table, hipStream_t stream) {
+hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
+                           int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
+                           const RopeMode& mode, const RopeTable& table, const RopeInner& inner,
+                           hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's error
-  const int64_t threads = n_tokens * (head_dim / 8);
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(pack_rope_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, src,
-                     dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, table);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope(uint16_t* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
-                       int64_t batch, int32_t heads, int32_t head_dim, const RopeTable& table,
-                       hipStream_t stream) {
-  (void)hipGetLastError();  // report only this launch's error
-  const int64_t threads = n_tokens * (head_dim / 8);
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, x,
-                     pos, n_tokens, axes, batch, heads, head_dim, table);
-  return hipGetLastError();
+  if (mode.split)
+    return mode.f64 ? launch_mode<true, true>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
+                                              table, inner, stream)
+                    : launch_mode<true, false>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks,
+                                               mode, table, inner, stream);
+  return mode.f64 ? launch_mode<false, true>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
+                                             table, inner, stream)
+                  : launch_mode<false, false>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
+                                              table, inner, stream);
 }
 
 }  // namespace ltxa

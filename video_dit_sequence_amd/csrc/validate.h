@@ -169,4 +169,33 @@ inline int check_attn_unpack(const void* q, const void* k, const void* v, const 
                     nk_valid, scale);
 }
 
+// Options of the rotary variants; opts may be NULL (all zero).
+inline int check_rope_opts(const ltxa_rope_opts* opts, int32_t heads, int32_t head_dim, int32_t axes) {
+  if (!opts) return LTXA_OK;
+  if (!(opts->rope_type == LTXA_ROPE_INTERLEAVED || opts->rope_type == LTXA_ROPE_SPLIT)) return LTXA_E_SHAPE;
+  if (!(opts->fp64_angles == 0 || opts->fp64_angles == 1)) return LTXA_E_SHAPE;
+  if (!(opts->middle == 0 || opts->middle == 1)) return LTXA_E_SHAPE;
+  if (opts->reserved != 0) return LTXA_E_SHAPE;
+  if (opts->grid_heads < 0 || opts->head_offset < 0) return LTXA_E_SHAPE;
+  if (opts->grid_heads > 0) {
+    if (int64_t(opts->head_offset) + heads > opts->grid_heads) return LTXA_E_SHAPE;
+    if (int64_t(opts->grid_heads) * (head_dim / 2) / axes < 1) return LTXA_E_SHAPE;
+    if (int64_t(opts->grid_heads) * (head_dim / 2) >= (INT64_C(1) << 40)) return LTXA_E_RANGE;
+    if (heads > 65535) return LTXA_E_RANGE;  // grid y of the per-head kernel
+  }
+  if (opts->rope_type == LTXA_ROPE_SPLIT && head_dim % 16 != 0) return LTXA_E_ALIGN;
+  return LTXA_OK;
+}
+
+// One tensor rotated in place: x [batch, n_tokens, heads, head_dim] bf16.
+inline int check_rope_ex(const void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                         const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, double theta,
+                         const ltxa_rope_opts* opts) {
+  if (!x) return LTXA_E_NULL;
+  const int rc = check_rope(x, pos, n_tokens, axes, max_pos, nullptr, nullptr, 0, 0, nullptr, batch, heads,
+                            head_dim, theta);
+  if (rc) return rc;
+  return check_rope_opts(opts, heads, head_dim, axes);
+}
+
 }  // namespace ltxa

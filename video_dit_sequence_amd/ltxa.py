@@ -34,7 +34,31 @@ LTXA_E_HIP = -6
 LTXA_E_RANGE = -7
 
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
-           "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack")
+           "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
+           "ltxa_rope_ex", "ltxa_sp_pack_rope_ex")
+
+LTXA_ROPE_INTERLEAVED = 0
+LTXA_ROPE_SPLIT = 1
+
+
+class RopeOpts(ctypes.Structure):
+    """``ltxa_rope_opts``: the rotary variants (see ``include/ltxa.h``)."""
+    _fields_ = [("rope_type", ctypes.c_int32), ("grid_heads", ctypes.c_int32),
+                ("head_offset", ctypes.c_int32), ("fp64_angles", ctypes.c_int32),
+                ("middle", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def rope_opts(rope_type: str = "interleaved", grid_heads: int = 0, head_offset: int = 0,
+              fp64_angles: bool = False, middle: bool = False) -> RopeOpts:
+    """Build an ``ltxa_rope_opts``.  ``rope_type`` is "interleaved" or "split";
+    ``grid_heads = 0`` shares one head_dim-wide grid across heads, ``G > 0``
+    lays the grid over ``G`` heads (head ``j`` of a tensor is grid head
+    ``head_offset + j``)."""
+    types = {"interleaved": LTXA_ROPE_INTERLEAVED, "split": LTXA_ROPE_SPLIT}
+    if rope_type not in types:
+        raise ValueError("rope_type must be 'interleaved' or 'split'")
+    return RopeOpts(types[rope_type], int(grid_heads), int(head_offset), int(bool(fp64_angles)),
+                    int(bool(middle)), 0)
 
 
 class LtxaError(RuntimeError):
@@ -74,6 +98,12 @@ def lib() -> ctypes.CDLL:
         L.ltxa_sp_pack_rope.restype = ctypes.c_int
         L.ltxa_sp_pack_rope.argtypes = [vp, vp, vp, i64, i32, dp, i64, i32, i32, i32,
                                         ctypes.c_double, vp]
+        op = ctypes.POINTER(RopeOpts)
+        L.ltxa_rope_ex.restype = ctypes.c_int
+        L.ltxa_rope_ex.argtypes = [vp, vp, i64, i32, dp, i64, i32, i32, ctypes.c_double, op, vp]
+        L.ltxa_sp_pack_rope_ex.restype = ctypes.c_int
+        L.ltxa_sp_pack_rope_ex.argtypes = [vp, vp, vp, i64, i32, dp, i64, i32, i32, i32,
+                                           ctypes.c_double, op, vp]
         L.ltxa_attn_fwd_unpack.restype = ctypes.c_int
         L.ltxa_attn_fwd_unpack.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                            ctypes.c_float, i32, vp]
@@ -204,12 +234,31 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Option
     return out
 
 
-def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
-                 theta: float = 10000.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` (``ltxa_sp_pack_rope``).
+def rope(x: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
+         opts: Optional[RopeOpts] = None) -> None:
+    """Rotate bf16 ``x`` (``[B, N, H, D]``) in place with the variants of
+    ``opts`` (:func:`rope_opts`; ``None`` = the rotation of :func:`rope_qk`)
+    (``ltxa_rope_ex``)."""
+    _gpu(x, "x", torch.bfloat16)
+    _gpu(pos, "pos", torch.int32)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, D]")
+    B, N, H, D = x.shape
+    if pos.dim() != 2 or pos.shape[0] != N or pos.shape[1] != len(max_pos):
+        raise ValueError("pos must be [N, A] with one max_pos per axis")
+    _check("ltxa_rope_ex", lib().ltxa_rope_ex(
+        x.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos), B, H, D, float(theta),
+        None if opts is None else ctypes.byref(opts), _stream_ptr(x)))
 
-    Equal, bit for bit, to :func:`sp_pack` followed by :func:`rope_qk` on the
-    packed tensor.  ``pos`` is an int32 ``[N, A]`` GPU tensor.
+
+def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
+                 theta: float = 10000.0, out: Optional[torch.Tensor] = None,
+                 opts: Optional[RopeOpts] = None) -> torch.Tensor:
+    """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` (``ltxa_sp_pack_rope``,
+    or ``ltxa_sp_pack_rope_ex`` when ``opts`` is given).
+
+    Equal, bit for bit, to :func:`sp_pack` followed by the rotation of each
+    rank's shard.  ``pos`` is an int32 ``[N, A]`` GPU tensor.
     """
     _gpu(src, "src", torch.bfloat16)
     _gpu(pos, "pos", torch.int32)
@@ -224,9 +273,14 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
     _gpu(out, "out", torch.bfloat16)
     if out.numel() != src.numel():
         raise ValueError("out has the wrong number of elements")
-    _check("ltxa_sp_pack_rope", lib().ltxa_sp_pack_rope(
-        src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
-        B, H, D, P, float(theta), _stream_ptr(src)))
+    if opts is None:
+        _check("ltxa_sp_pack_rope", lib().ltxa_sp_pack_rope(
+            src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
+            B, H, D, P, float(theta), _stream_ptr(src)))
+    else:
+        _check("ltxa_sp_pack_rope_ex", lib().ltxa_sp_pack_rope_ex(
+            src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
+            B, H, D, P, float(theta), ctypes.byref(opts), _stream_ptr(src)))
     return out
 
 

@@ -20,6 +20,19 @@ for the full-resolution distilled call, and a 32768-token cap):
 * ``cross_24576x1000`` -- video queries 12x32x64 = 24576 (3-axis positions)
                        against 1000 audio keys (1-axis positions) padded to
                        1024; 4 heads (of 32) of 64 channels.
+* ``connector_1024`` -- the text connector's 1D self-attention (FastVideo
+                       gemma page, ``Embeddings1DConnector``): 1024 text
+                       tokens at positions 0..1023, 32 heads of 128, batch
+                       2.  Its rotary grid spans the inner dimension (32
+                       heads x 128).  With learnable registers every slot is
+                       valid (the mask is reset to zeros), so all 1024 keys
+                       attend.
+* ``connector_1024_masked`` -- the same without registers: an additive mask
+                       whose valid prefix is 700 tokens, i.e. ``nk_valid`` =
+                       700; batch 1.
+
+The pages print no connector sizes; 1024 tokens, 32 x 128 and max_pos 1024
+are this library's choices.
 
 Values: independent N(0, 1) draws from ``torch.Generator('cpu')`` seeded per
 workload, rounded to bfloat16 (round to nearest even).  Q, K and V are drawn
@@ -47,14 +60,17 @@ class Workload:
     q_grid: Tuple[int, int, int]
     q_extra: int            # extra tokens appended on the t = T plane
     q_max_pos: Tuple[float, ...]
-    k_kind: str             # "video" (same positions as the queries) or "audio"
+    k_kind: str             # "video" (same positions as the queries), "audio" or "text"
     k_max_pos: Tuple[float, ...]
     full_heads: int         # heads of the token-major tensor before the exchange
     world_sizes: Tuple[int, ...] = field(default=(1,))
     theta: float = 10000.0
+    q_kind: str = "video"   # "video": 3-axis grid positions; "text": 1-axis 0..nq-1
 
     @property
     def nq_valid(self) -> int:
+        if self.q_kind == "text":
+            return self.nk_valid
         t, x, y = self.q_grid
         return t * x * y + self.q_extra
 
@@ -89,6 +105,16 @@ WORKLOADS = {
         nq=24576, nk_pad=1024, nk_valid=1000, q_grid=(12, 32, 64), q_extra=0,
         q_max_pos=(12, 32, 64), k_kind="audio", k_max_pos=(1000,),
         full_heads=32, world_sizes=(8,)),
+    "connector_1024": Workload(
+        name="connector_1024", seed=1005, B=2, heads=32, head_dim=128,
+        nq=1024, nk_pad=1024, nk_valid=1024, q_grid=(1, 1, 1024), q_extra=0,
+        q_max_pos=(1024,), k_kind="text", k_max_pos=(1024,),
+        full_heads=32, world_sizes=(1,), q_kind="text"),
+    "connector_1024_masked": Workload(
+        name="connector_1024_masked", seed=1006, B=1, heads=32, head_dim=128,
+        nq=1024, nk_pad=1024, nk_valid=700, q_grid=(1, 1, 1024), q_extra=0,
+        q_max_pos=(1024,), k_kind="text", k_max_pos=(1024,),
+        full_heads=32, world_sizes=(1,), q_kind="text"),
 }
 
 
@@ -123,6 +149,11 @@ def audio_positions(n_valid: int, n_total: Optional[int] = None) -> np.ndarray:
 
 def positions(w: Workload):
     """``(q_pos, k_pos)`` for a workload, covering ``nq`` / ``nk_pad`` rows."""
+    if w.q_kind == "text":
+        # Every slot of the text sequence has its index as position (the
+        # connector rotates by arange over the sequence, padding included).
+        q_pos = audio_positions(w.nq, w.nq)
+        return q_pos, audio_positions(w.nk_pad, w.nk_pad)
     q_pos = video_positions(w.q_grid, w.q_extra, w.nq)
     if w.k_kind == "video":
         k_pos = video_positions(w.q_grid, w.q_extra, w.nk_pad)
