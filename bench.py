@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
+    ap.add_argument("--secondary", type=int, default=1,
+                    help="also time the cross-attention and connector workloads (reported apart)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 skips it)")
     return ap.parse_args()
@@ -103,6 +105,75 @@ def cpu_baseline(w, q, k, v, qpos, kpos, budget_s):
             "sample": f"{done_rows} query rows over {heads_used} head(s) x {w.nk_valid} keys, "
                       f"head_dim {w.head_dim}, fp64 numpy (rotary + attention), {dt:.1f} s",
             "host_cpus": os.cpu_count()}
+
+
+def secondary(ltxa, wl, dev, iters):
+    """Time the other instantiations of the path (not part of ``value``):
+    video->audio cross-attention for all 8 ranks of the 32-head share (fused
+    pack+rotary of the video Q and audio K, pack of V, attention into token
+    order), and the 1D text connector's attention core (rotary over the
+    inner dimension on Q and K, then attention over all 32 heads)."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    w = wl.WORKLOADS["cross_24576x1000"]
+    P, H = w.world_sizes[0], w.full_heads
+    q, k, v = (t.to(dev) for t in wl.qkv(w, heads=H))
+    qp, kp = (torch.from_numpy(p).to(dev) for p in wl.positions(w))
+    qs = torch.empty((P, w.B, w.nq, H // P, w.head_dim), dtype=torch.bfloat16, device=dev)
+    ks = torch.empty((P, w.B, w.nk_pad, H // P, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vs, o = torch.empty_like(ks), torch.empty_like(q)
+
+    def cross():
+        ltxa.sp_pack_rope(q, qp, w.q_max_pos, P, w.theta, out=qs)
+        ltxa.sp_pack_rope(k, kp, w.k_max_pos, P, w.theta, out=ks)
+        ltxa.sp_pack(v, P, out=vs)
+        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o)
+
+    def cross_attn_only():
+        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o)
+
+    flop = 4.0 * w.nq * w.nk_valid * w.head_dim * H * w.B
+    ms, ams = timed(cross), timed(cross_attn_only)
+    out["cross_24576x1000"] = {"ms_per_step": round(ms, 4), "attn_ms": round(ams, 4),
+                               "attn_tflops": round(flop / (ams * 1e-3) / 1e12, 1),
+                               "attn_frac_bf16_peak": round(flop / (ams * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "flop_per_step": flop, "heads": H, "virtual_ranks": P}
+    del q, k, v, qs, ks, vs, o
+
+    w = wl.WORKLOADS["connector_1024"]
+    q, k, v = (t.to(dev) for t in wl.qkv(w))
+    pos = torch.from_numpy(wl.positions(w)[0]).to(dev)
+    o = torch.empty_like(q)
+    opts = ltxa.rope_opts(grid_heads=w.heads)
+
+    def connector():
+        ltxa.rope(q, pos, w.q_max_pos, w.theta, opts=opts)
+        ltxa.rope(k, pos, w.k_max_pos, w.theta, opts=opts)
+        ltxa.attn_fwd(q, k, v, nk_valid=w.nk_valid, out=o)
+
+    def connector_attn_only():
+        ltxa.attn_fwd(q, k, v, nk_valid=w.nk_valid, out=o)
+
+    flop = 4.0 * w.nq * w.nk_valid * w.head_dim * w.heads * w.B
+    ms, ams = timed(connector), timed(connector_attn_only)
+    out["connector_1024"] = {"ms_per_step": round(ms, 4), "attn_ms": round(ams, 4),
+                             "attn_tflops": round(flop / (ams * 1e-3) / 1e12, 1),
+                             "attn_frac_bf16_peak": round(flop / (ams * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "flop_per_step": flop, "heads": w.heads, "batch": w.B}
+    return out
 
 
 def main():
@@ -226,6 +297,8 @@ def main():
                         for k_ in phase_names if k_ in phase_bytes}, "peak": PEAK_HBM_GBS},
         "device": torch.cuda.get_device_name(0),
     }
+    if args.secondary:
+        line["secondary"] = secondary(ltxa, wl, dev, 20)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, qpos, kpos, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -396,3 +396,24 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     os_ = attn_fwd(qs, ks, vs, nk_valid=nk_valid, scale=scale)
     out = sp_unpack(os_.view(P, B, N, Hl, D))
     return out[:, :share.n_valid]
+
+
+def connector_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, max_pos,
+                        nk_valid: Optional[int] = None, theta: float = 10000.0,
+                        rope_type: str = "interleaved", fp64_angles: bool = False,
+                        scale: Optional[float] = None) -> torch.Tensor:
+    """The attention core of the 1D text connector (FastVideo gemma page,
+    ``Embeddings1DConnector.forward``): rotate Q and K in place by 1D
+    positions with the grid over the inner dimension (all ``H`` heads,
+    ``num_attention_heads = H``), then masked attention over every head.
+
+    ``q``, ``k``, ``v``: bf16 ``[B, N, H, D]`` on one GPU (no sequence
+    parallelism); ``pos``: int32 ``[N, 1]``; an additive mask with a valid
+    prefix of ``nk_valid`` keys is ``nk_valid`` (default: all keys, as after
+    the learnable registers replace the padding).  Returns ``[B, N, H, D]``.
+    """
+    H = q.shape[2]
+    opts = rope_opts(rope_type=rope_type, grid_heads=H, fp64_angles=fp64_angles)
+    rope(q, pos, max_pos, theta, opts=opts)
+    rope(k, pos, max_pos, theta, opts=opts)
+    return attn_fwd(q, k, v, nk_valid=nk_valid, scale=scale)
