@@ -48,9 +48,10 @@
 // in the token-major layout the head shards came from.
 //
 // Masking.  Only the one tile that straddles nk_valid is masked (scores of
-// keys >= nk_valid set to -inf).  Its K/V rows past nk_valid are loaded from
-// row nk_valid-1 instead, so no padded value (NaN included) is ever read;
-// tiles wholly past nk_valid are not visited.
+// keys >= nk_valid set to -inf).  Its copy goes through a buffer resource
+// whose extent ends at key nk_valid - 1, so rows past it arrive as zeros and
+// no padded value (NaN included) is ever read; tiles wholly past nk_valid
+// are not visited.
 #include <cmath>
 
 #include "common.h"
