@@ -92,3 +92,24 @@ def test_rope_rejects_bad_arguments():
         ltxa.rope_qk(x, pos, (1, 0, 1), None, None, None)
     with pytest.raises(ltxa.LtxaError):
         ltxa.rope_qk(x, pos, (1, 1, 1), x, pos, (1, 1, 1))  # q and k alias
+
+
+@pytest.mark.parametrize("B,H,D,P", [(2, 3, 24, 3), (1, 5, 40, 5), (2, 2, 256, 2), (3, 6, 64, 3)])
+def test_odd_shapes_match_oracle_and_pack_fusion(B, H, D, P):
+    # Head widths whose 16-byte groups do not divide a wave (24, 40), the
+    # widest head (256), batches > 1, and the fused pack on each.
+    print(f"rope odd shape B={B} H={H} D={D} P={P}", flush=True)
+    g = torch.Generator().manual_seed(1000 + D)
+    N = 6 * 7 * 5
+    x = wl.randn_bf16((B, N, H, D), g)
+    pos = wl.video_positions((6, 7, 5))
+    pg = torch.from_numpy(pos).to(DEV)
+    xg = x.to(DEV)
+    ltxa.rope_qk(xg, pg, (6, 7, 5), None, None, None)
+    fused = ltxa.sp_pack_rope(x.to(DEV), pg, (6, 7, 5), P)
+    torch.cuda.synchronize()
+    ref = oracle.rope_apply(f64(x), pos, (6, 7, 5), 10000.0)
+    ok, exact = rope_ok(f64(xg), ref, f64(x))
+    assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
+    assert exact > 0.995
+    assert np.array_equal(bits(fused), bits(ltxa.sp_pack(xg, P)))

@@ -19,7 +19,10 @@
 //    pairs (split: 16 bytes in each half of the head).  It computes the
 //    cos/sin of its pairs once and applies them to every (batch, head) row
 //    of that token, so the transcendentals are amortised over batch * heads
-//    rows.  Lanes cover consecutive groups of consecutive tokens.
+//    rows.  Lanes cover consecutive groups of consecutive tokens.  Loads and
+//    stores are non-temporal: each byte is touched once.  (A mapping with
+//    whole token rows per wave, which reads 1 KiB per instruction, measured
+//    slower: it repeats the cos/sin for every head group.)
 //  * Inner grid (heads turn at different frequencies).  One thread owns one
 //    head and one pair group for a run of tokens: its frequencies are
 //    computed once (fp64 pow) and reused across the run; the cos/sin are
@@ -100,24 +103,25 @@ __device__ __forceinline__ void rotate_rows(const RowAddr* a, int count, int g, 
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u)
       if (u < count) {
-        lo[u] = *reinterpret_cast<const u32x4*>(a[u].src + 8 * g);
-        hi[u] = *reinterpret_cast<const u32x4*>(a[u].src + half + 8 * g);
+        lo[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a[u].src + 8 * g));
+        hi[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a[u].src + half + 8 * g));
       }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u)
       if (u < count) {
         rotate_split(lo[u], hi[u], c, s);
-        *reinterpret_cast<u32x4*>(a[u].dst + 8 * g) = lo[u];
-        *reinterpret_cast<u32x4*>(a[u].dst + half + 8 * g) = hi[u];
+        __builtin_nontemporal_store(lo[u], reinterpret_cast<u32x4*>(a[u].dst + 8 * g));
+        __builtin_nontemporal_store(hi[u], reinterpret_cast<u32x4*>(a[u].dst + half + 8 * g));
       }
   } else {
     u32x4 w[kRowsInFlight];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u)
-      if (u < count) w[u] = *reinterpret_cast<const u32x4*>(a[u].src + 8 * g);
+      if (u < count) w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a[u].src + 8 * g));
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u)
-      if (u < count) *reinterpret_cast<u32x4*>(a[u].dst + 8 * g) = rotate_interleaved(w[u], c, s);
+      if (u < count)
+        __builtin_nontemporal_store(rotate_interleaved(w[u], c, s), reinterpret_cast<u32x4*>(a[u].dst + 8 * g));
   }
 }
 

@@ -53,9 +53,10 @@ inline int check_perm(const void* src, const void* dst, int64_t batch, int64_t n
   int64_t bytes = mul4_capped(batch, n_tokens, heads, mul_capped(head_dim, elem_bytes));
   if (bytes < 0) return LTXA_E_RANGE;
   int64_t chunk = static_cast<int64_t>(heads / world_size) * head_dim * elem_bytes;
-  // Grid: y = world_size (<= 65535); x counts 16-byte vectors per rank slab.
+  // Grid: one thread per vector (1 to 16 bytes), 256 per workgroup, at most
+  // 2^31 - 1 workgroups: 2^38 bytes (256 GiB) per tensor always fits.
   if (world_size > 65535) return LTXA_E_RANGE;
-  if (bytes / world_size > (INT64_C(1) << 40)) return LTXA_E_RANGE;
+  if (bytes > (INT64_C(1) << 38)) return LTXA_E_RANGE;
   if (overlap(src, bytes, dst, bytes)) return LTXA_E_ALIAS;
   plan->bytes = bytes;
   plan->rows = batch * n_tokens;
