@@ -283,6 +283,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     // block i % 2 at channel step i / 2, so consecutive products are
     // independent; reads run kKAhead fragments ahead of the products.
     f32x16 sc[2] = {neg_m, neg_m};
+    // Matrix sections run at raised wave priority: when the other wave on
+    // this SIMD is in its softmax, its vector instructions fill the cycles
+    // between these products instead of delaying them.
+    __builtin_amdgcn_s_setprio(1);
     {
       bf16x8 kf[2 * KS];
 #pragma unroll
@@ -298,6 +302,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKAhead, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (decltype(masked)::value != 0) {
       // Key of register r in block kb is 32kb + 8(r/4) + 4hf + r%4: compare
       // its lane-independent part against the lane's limit.
@@ -308,9 +314,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r)
           if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
     }
+    // Tile max as a chain of three-input maxima (one instruction per two scores).
     float a = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) a = fmaxf(a, fmaxf(sc[0][r], sc[1][r]));
+    for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sc[0][r]), sc[1][r]);
     const float mx = fmaxf(a, partner(a));  // tile max, relative to m
     if (__builtin_amdgcn_ballot_w64(t == 0 || mx > kRescaleSlack)) {
       // First tile: m becomes its max.  Later: raise m to the new max (when
@@ -352,6 +359,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       }
       return pg;
     };
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 pf[4];
     bf16x8 vf[4 * DB];
 #pragma unroll
@@ -374,6 +382,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       if (i + kVAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       if (i < 3 * DB) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerGroup / DB, 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   char* const ringK[kStages] = {sK0, sK1};
