@@ -86,6 +86,8 @@ constexpr int kBufferFlags = 0x00020000;
 // lgkmcnt 11:8).
 constexpr short kWaitVm[16] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75, 0x0F76, 0x0F77,
                                0x0F78, 0x0F79, 0x0F7A, 0x0F7B, 0x0F7C, 0x0F7D, 0x0F7E, 0x0F7F};
+// s_waitcnt immediate for lgkmcnt(0), vmcnt and expcnt at their maxima.
+constexpr short kWaitLgkm0 = static_cast<short>(0xC07F);
 
 template <int N>
 struct Int {
@@ -154,17 +156,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) char sK0[TILE], sK1[TILE];
   __shared__ __attribute__((aligned(1024))) char sV0[TILE], sV1[TILE];
 
-  // Bytes a copy leaves unwritten must not hold stale NaN patterns: start
-  // the ring at zero.
-  {
-    char* const ring[4] = {sK0, sK1, sV0, sV1};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int off = threadIdx.x * 16; off < TILE; off += kThreads * 16)
-        *reinterpret_cast<u32x4*>(ring[i] + off) = u32x4{};
-  }
-
   const int lid = xcd_contiguous(blockIdx.x, nblocks);
   const int bh = lid / qblocks;
   const int qb = lid - bh * qblocks;
@@ -189,6 +180,54 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   float* lbase = lse ? lse + (b * heads + h) * nq : nullptr;
   asm volatile("" : "+s"(obase), "+s"(lbase));
   const int64_t ors = int64_t(out_heads) * D;  // elements between output tokens
+
+  // Tile copy: DMA instruction j of this wave fills LDS bytes
+  // [(wave*LOADS + j) * 1024, +1024); lane l writes 16-byte slot
+  // s = (wave*LOADS + j)*64 + l = (row s / CH, position s % CH), which holds
+  // the row's global chunk (position ^ swz(row)).  The copy goes through a
+  // buffer resource whose extent ends with the last valid key: rows past it
+  // read as zeros, so the padded keys are never touched.
+  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
+  const int full_tiles = static_cast<int>(nk_valid / kBK);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t cp_off[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int s = (wave * LOADS + j) * 64 + lane;
+    const int row = s / CH;
+    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
+  }
+  auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
+    const int64_t first = int64_t(t) * kBK;
+    const int64_t rows = nk_valid - first < kBK ? nk_valid - first : kBK;
+    const uint32_t extent = static_cast<uint32_t>((rows - 1) * rs * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbase + first * rs, extent);
+    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbase + first * rs, extent);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + j) * 1024);
+      LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + j) * 1024);
+      dma16(rk, kd, cp_off[j]);
+      dma16(rv, vd, cp_off[j]);
+    }
+  };
+
+  // Bytes a copy leaves unwritten must not hold stale NaN patterns (a V row
+  // past nk_valid meets a zero probability, and 0 * NaN is NaN): each lane
+  // first zeroes the 16-byte slots its own copies fill, in every stage, and
+  // waits for those stores before its first copy, so no ordering between
+  // waves is needed.  Tile 0 is then requested before Q is read, so that
+  // the two loads' latencies overlap.
+  {
+    char* const ring[4] = {sK0, sK1, sV0, sV1};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        *reinterpret_cast<u32x4*>(ring[i] + (wave * LOADS + j) * 1024 + lane * 16) = u32x4{};
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+  issue_tile(0, sK0, sV0);
 
   // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
   const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
@@ -225,37 +264,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       v_off1[d] = (v_row0 + 8) * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x1) << 4);
     }
   }
-
-  // Tile copy: DMA instruction j of this wave fills LDS bytes
-  // [(wave*LOADS + j) * 1024, +1024); lane l writes 16-byte slot
-  // s = (wave*LOADS + j)*64 + l = (row s / CH, position s % CH), which holds
-  // the row's global chunk (position ^ swz(row)).  The copy goes through a
-  // buffer resource whose extent ends with the last valid key: rows past it
-  // read as zeros, so the padded keys are never touched.
-  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
-  const int full_tiles = static_cast<int>(nk_valid / kBK);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t cp_off[LOADS];
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int s = (wave * LOADS + j) * 64 + lane;
-    const int row = s / CH;
-    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
-  }
-  auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
-    const int64_t first = int64_t(t) * kBK;
-    const int64_t rows = nk_valid - first < kBK ? nk_valid - first : kBK;
-    const uint32_t extent = static_cast<uint32_t>((rows - 1) * rs * 2 + D * 2);
-    const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbase + first * rs, extent);
-    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbase + first * rs, extent);
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + j) * 1024);
-      LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + j) * 1024);
-      dma16(rk, kd, cp_off[j]);
-      dma16(rv, vd, cp_off[j]);
-    }
-  };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -403,7 +411,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 
   // Steady state: pairs of wholly valid tiles, no masking.  Then at most one
   // more full tile and the one tile that straddles nk_valid.
-  issue_tile(0, ringK[0], ringV[0]);
   int t = 0;
   for (; t + 2 <= full_tiles; t += 2) {
     iteration(t, Int<0>{}, Int<0>{});
