@@ -25,7 +25,7 @@
 //    slower: it repeats the cos/sin for every head group.)
 //  * Inner grid (heads turn at different frequencies).  One thread owns one
 //    head and one pair group for a run of tokens: its frequencies are
-//    computed once (fp64 pow) and reused across the run; the cos/sin are
+//    computed once (fp64 pow) and reused across the run of 4 tokens; the cos/sin are
 //    per token.  Lanes cover the groups of one head row, then tokens.
 #include "common.h"
 #include "kernels.h"
@@ -35,7 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsInFlight = 4;
-constexpr int kInnerTokensPerThread = 8;
+constexpr int kInnerTokensPerThread = 4;
 
 // cos/sin of the angle (pos + mid) * coef; fp32 or fp64 evaluation.
 template <bool F64>
