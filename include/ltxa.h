@@ -135,8 +135,10 @@ int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
  *   nk_valid are never read, so their contents (NaN included) cannot reach
  *   the output.  Query rows past the caller's valid length are computed like
  *   any other row.
- * Arithmetic: bf16 products with fp32 accumulation, fp32 online softmax,
- * fp32 -> bf16 output rounding (nearest even).
+ * Arithmetic: q is multiplied by scale * log2(e) and rounded to bf16 once
+ * (relative error <= 2^-9 per element, so logits move by at most 2^-9 of
+ * sum_d |q_d k_d| * scale); then bf16 products with fp32 accumulation, fp32
+ * online softmax in base 2, fp32 -> bf16 output rounding (nearest even).
  * Errors: E_NULL (q, k, v or o NULL); E_SHAPE (batch, heads, nq < 1;
  * head_dim not 64 or 128; nk_valid not in [1, nk_pad]; scale not finite and
  * > 0); E_ALIGN (a pointer not 16-byte aligned); E_ALIAS (o or lse overlaps

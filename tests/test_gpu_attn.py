@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle
-from parity import LSE_ABS, assert_attn_close, bits, f64
+from parity import (ATTN_COSINE, ATTN_REL_RMS, LSE_ABS, assert_attn_close, attn_errors, bf16_round, bits,
+                    f64)
 from video_dit_sequence_amd import ltxa
 from video_dit_sequence_amd import workloads as wl
 
@@ -166,3 +167,45 @@ def test_attn_rejects_bad_arguments():
     assert L.ltxa_attn_fwd(p, p, p, o.data_ptr(), None, 1, 2, 96, 64, 64, 64, 0.1, None) == ltxa.LTXA_E_SHAPE
     assert L.ltxa_attn_fwd(p, p, p, p, None, 1, 2, 128, 64, 64, 64, 0.1, None) == ltxa.LTXA_E_ALIAS
     assert L.ltxa_attn_fwd(p + 2, p, p, o.data_ptr(), None, 1, 2, 128, 64, 64, 64, 0.1, None) == ltxa.LTXA_E_ALIGN
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "wide"])
+def test_running_max_rescale_paths(pattern):
+    # The kernel raises its running max only when a tile exceeds it by more
+    # than a slack, then rescales what it has accumulated.  Rising key norms
+    # force a raise on most tiles; falling norms never raise after the first
+    # tile; a large scale spreads the scores so that most probabilities are
+    # tiny next to the largest ones.
+    print(f"attn rescale {pattern}", flush=True)
+    g = torch.Generator().manual_seed({"rising": 11, "falling": 12, "wide": 13}[pattern])
+    nq, nk, D = 300, 1000, 128
+    q = wl.randn_bf16((1, nq, 2, D), g)
+    k = wl.randn_bf16((1, nk, 2, D), g).to(torch.float32)
+    v = wl.randn_bf16((1, nk, 2, D), g)
+    j = torch.arange(nk, dtype=torch.float32)[None, :, None, None]
+    scale = 1.0 / np.sqrt(D)
+    if pattern == "rising":
+        k = k * (0.25 + j / 100.0)
+    elif pattern == "falling":
+        k = k * (10.25 - j / 100.0)
+    else:
+        scale = 0.35   # scores with std ~4 (log2 units ~6): probabilities span ~2^-60 .. 1
+    k = k.to(torch.bfloat16)
+    nkv = nk - 3
+    o, L = _run(q, k, v, nkv, scale)
+    got = f64(o)
+    # Against the plain oracle: the relative bars (the absolute ones are
+    # defined for unit-variance logits, and these logits reach far beyond).
+    ref, _ = oracle.attention(f64(q), f64(k), f64(v), nkv, scale)
+    e = attn_errors(got, ref)
+    print(f"rescale/{pattern}: {e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert e["rel_rms"] <= ATTN_REL_RMS and e["cosine"] >= ATTN_COSINE, e
+    # Against the oracle on the operands as the ABI documents the kernel
+    # rounds them (scale * log2(e) * q rounded to bf16 once): the full bar,
+    # absolute bounds included, and the log-sum-exp bar.
+    log2e = 1.4426950408889634
+    q_r = bf16_round(f64(q) * scale * log2e) / log2e
+    ref_r, lse_r = oracle.attention(q_r, f64(k), f64(v), nkv, 1.0)
+    assert_attn_close(got, ref_r, f"rescale/{pattern} (rounded q)")
+    assert np.max(np.abs(f64(L) - lse_r)) <= LSE_ABS
