@@ -169,15 +169,18 @@ def test_attn_rejects_bad_arguments():
     assert L.ltxa_attn_fwd(p + 2, p, p, o.data_ptr(), None, 1, 2, 128, 64, 64, 64, 0.1, None) == ltxa.LTXA_E_ALIGN
 
 
-@pytest.mark.parametrize("pattern", ["rising", "falling", "wide"])
+@pytest.mark.parametrize("pattern", ["rising", "steep", "falling", "wide"])
 def test_running_max_rescale_paths(pattern):
-    # The kernel raises its running max only when a tile exceeds it by more
-    # than a slack, then rescales what it has accumulated.  Rising key norms
-    # force a raise on most tiles; falling norms never raise after the first
-    # tile; a large scale spreads the scores so that most probabilities are
-    # tiny next to the largest ones.
+    # The kernel keeps the first tile's row max as its softmax offset m and
+    # raises it only when a lane's tile sum of probabilities exceeds 2^64,
+    # then rescales what it has accumulated and recomputes the tile.  Rising
+    # key norms (up to 10x) push later scores ~30 log2 units above m without
+    # tripping the guard; steep norms (up to 40x) push them past 64 log2
+    # units, so the guard fires, on many tiles; falling norms keep every
+    # later score below m; a large scale spreads the scores so that most
+    # probabilities are tiny next to the largest ones.
     print(f"attn rescale {pattern}", flush=True)
-    g = torch.Generator().manual_seed({"rising": 11, "falling": 12, "wide": 13}[pattern])
+    g = torch.Generator().manual_seed({"rising": 11, "steep": 14, "falling": 12, "wide": 13}[pattern])
     nq, nk, D = 300, 1000, 128
     q = wl.randn_bf16((1, nq, 2, D), g)
     k = wl.randn_bf16((1, nk, 2, D), g).to(torch.float32)
@@ -186,6 +189,8 @@ def test_running_max_rescale_paths(pattern):
     scale = 1.0 / np.sqrt(D)
     if pattern == "rising":
         k = k * (0.25 + j / 100.0)
+    elif pattern == "steep":
+        k = k * (0.25 + j / 25.0)
     elif pattern == "falling":
         k = k * (10.25 - j / 100.0)
     else:
@@ -194,13 +199,15 @@ def test_running_max_rescale_paths(pattern):
     nkv = nk - 3
     o, L = _run(q, k, v, nkv, scale)
     got = f64(o)
-    # Against the plain oracle: the relative bars (the absolute ones are
-    # defined for unit-variance logits, and these logits reach far beyond).
+    # Against the plain oracle: a sanity bound (the bars are defined for
+    # unit-variance logits; these reach ~100 log2 units, where the one bf16
+    # rounding of the scaled q alone moves logits by ~0.2): relative RMS
+    # within twice the unit-variance bar, cosine at the bar.
     ref, _ = oracle.attention(f64(q), f64(k), f64(v), nkv, scale)
     e = attn_errors(got, ref)
     print(f"rescale/{pattern}: {e}", flush=True)
     assert np.all(np.isfinite(got))
-    assert e["rel_rms"] <= ATTN_REL_RMS and e["cosine"] >= ATTN_COSINE, e
+    assert e["rel_rms"] <= 2 * ATTN_REL_RMS and e["cosine"] >= ATTN_COSINE, e
     # Against the oracle on the operands as the ABI documents the kernel
     # rounds them (scale * log2(e) * q rounded to bf16 once): the full bar,
     # absolute bounds included, and the log-sum-exp bar.

@@ -38,10 +38,14 @@
 // Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once),
 // so the products are log2-domain scores, and every score product starts
 // from a register block holding -m: exp2 consumes the accumulator as is.
-// The running max m is only raised, and O and the row sum rescaled, when a
-// tile's max exceeds it by more than 8 (a factor of 256); until then exp2
-// arguments stay <= 8, far from overflow.  The row sum adds the
-// bf16-rounded probabilities that also feed the P*V product.
+// m is the first tile's row max and is not tracked per tile: the softmax is
+// invariant to the offset, and fp32/bf16 hold probabilities up to 2^127, so
+// m only has to rise when a probability could leave the safe range.  After
+// each tile's exponentials the lane's row sum is checked: above 2^64 (or not
+// finite), the tile's exact max becomes m, O and the sum are rescaled and
+// the tile's probabilities recomputed.  With the guard at 2^64, P <= 2^64,
+// O <= 2^64 * |v| * keys and the sum stay far inside fp32.  The row sum
+// adds the bf16-rounded probabilities that also feed the P*V product.
 //
 // Output.  Staged per wave through LDS and stored as whole rows (see the
 // end of the kernel); the row addressing also lets the output land directly
@@ -70,14 +74,12 @@ constexpr int kQW = 32;                // query rows per wave
 constexpr int kBQ = kWaves * kQW;      // query rows per workgroup
 constexpr int kBK = 64;                // keys per tile
 constexpr int kStages = 2;             // LDS ring depth
-constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr float kSumGuard = 18446744073709551616.0f;  // 2^64: a lane's tile row sum above it raises m
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kKAhead = 3;        // K fragments in flight ahead of the products
 constexpr int kVAhead = 2;        // V fragments in flight ahead of the products
-constexpr int kValuPerGroup = 16; // VALU ops per 16-key group of probabilities
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // chips: 32-bit data format, everything else zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -269,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
   // Softmax state.  m is the offset subtracted from every log2-domain score
-  // before exp2; it is the running max, raised only when a tile exceeds it
-  // by more than kRescaleSlack.  The score products start from a register
-  // block holding -m, so they come out already offset (no per-score VALU).
+  // before exp2: the first tile's max, raised only by the sum guard.  The
+  // score products start from a register block holding -m, so they come out
+  // already offset (no per-score VALU).
   float m = 0.0f;       // replaced by the first tile's max
   float l = 0.0f;       // running sum over this lane's keys
   f32x16 neg_m = f32x16{};
@@ -322,21 +324,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r)
           if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
     }
-    // Tile max as a chain of three-input maxima (one instruction per two scores).
-    float a = fmaxf(sc[0][0], sc[1][0]);
+    auto tile_max = [&] __device__() __attribute__((always_inline)) {
+      float a = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sc[0][r]), sc[1][r]);
-    const float mx = fmaxf(a, partner(a));  // tile max, relative to m
-    if (__builtin_amdgcn_ballot_w64(t == 0 || mx > kRescaleSlack)) {
-      // First tile: m becomes its max.  Later: raise m to the new max (when
-      // above it) and rescale what has been accumulated.
-      const float delta = t == 0 ? mx : fmaxf(mx, 0.0f);
-      if (t != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-      }
+      for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sc[0][r]), sc[1][r]);
+      return fmaxf(a, partner(a));  // tile max, relative to m
+    };
+    auto shift = [&] __device__(float delta) __attribute__((always_inline)) {
       m += delta;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -344,31 +338,44 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         sc[1][r] -= delta;
         neg_m[r] = -m;
       }
-    }
-
-    // P^T in bf16, 16 keys per operand: operand (2kb + j) holds registers
-    // 8j..8j+7 of block kb.  O^T += V^T * P^T one 16-key group at a time.
-    // Order: the exponentials of group G+1 are interleaved with the four
-    // products of group G, and V fragments are read two products ahead.
-    float sum = 0.0f;
-    auto probs = [&] __device__(int G) __attribute__((always_inline)) {
-      bf16x8 pg;
-      const int kb = G >> 1, j = G & 1;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e]);
-        const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e + 1]);
-        bf16x2 pp;
-        pp[0] = static_cast<__bf16>(p0);
-        pp[1] = static_cast<__bf16>(p1);
-        sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
-        pg[e] = pp[0];
-        pg[e + 1] = pp[1];
-      }
-      return pg;
     };
-    __builtin_amdgcn_s_setprio(1);
+    if (t == 0) shift(tile_max());   // the first tile sets m to its max
+    float sum = 0.0f;
     bf16x8 pf[4];
+    auto probs = [&] __device__() __attribute__((always_inline)) {
+      sum = 0.0f;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const int kb = G >> 1, j = G & 1;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e]);
+          const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e + 1]);
+          bf16x2 pp;
+          pp[0] = static_cast<__bf16>(p0);
+          pp[1] = static_cast<__bf16>(p1);
+          sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+          pf[G][e] = pp[0];
+          pf[G][e + 1] = pp[1];
+        }
+      }
+    };
+    probs();
+    // m is only raised when a probability could leave the safe range (a
+    // lane's sum above kSumGuard, or not finite).  Then the tile's exact max
+    // becomes the new m, the accumulated state is rescaled and the
+    // probabilities are recomputed; P*V has not consumed them yet.
+    if (__builtin_amdgcn_ballot_w64(!(sum <= kSumGuard))) {
+      const float delta = fmaxf(tile_max(), 0.0f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+      shift(delta);
+      probs();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 vf[4 * DB];
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
@@ -376,19 +383,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       vf[i] = lds_tr_pair(lV + G * 16 * ROW + v_off0[d], lV + G * 16 * ROW + v_off1[d]);
     }
 #pragma unroll
-    for (int G = 0; G < 4; ++G) pf[G] = probs(G);
-#pragma unroll
     for (int i = 0; i < 4 * DB; ++i) acc[i % DB] = mfma32(vf[i], pf[i / DB], acc[i % DB]);
     l += sum;
-    // Schedule: P(0) and the first reads, then per product: 1 MFMA, the next
-    // fragment's 2 transpose reads, and a share of the next group's exps.
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerGroup, 1);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVAhead, 1);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
       if (i + kVAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-      if (i < 3 * DB) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerGroup / DB, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
