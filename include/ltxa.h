@@ -68,7 +68,8 @@ const char* ltxa_status_string(int status);
  * Errors: E_NULL (src or dst NULL); E_SHAPE (a size < 1, or elem_bytes not in
  * {1,2,4,8}); E_DIVISIBILITY (heads % world_size != 0, or n_tokens %
  * world_size != 0: the SP page pads the sequence to a multiple of
- * world_size first); E_ALIAS (src and dst byte ranges overlap); E_RANGE.
+ * world_size first); E_ALIAS (src and dst byte ranges overlap); E_RANGE
+ * (a tensor above 2^38 bytes, or world_size above 65535).
  * Any pointer alignment is accepted; 16-byte aligned rows are fastest.
  */
 int ltxa_sp_pack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
