@@ -47,6 +47,9 @@ def parse():
                     help="also time the cross-attention and connector workloads (reported apart)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 skips it)")
+    ap.add_argument("--inputs", choices=("normal", "zeros"), default="normal",
+                    help="diagnostic only: 'zeros' runs the same step on all-zero Q/K/V, which "
+                         "shows how far the chip's clock under matrix load depends on the data")
     return ap.parse_args()
 
 
@@ -194,6 +197,9 @@ def main():
     q_cpu, k_cpu, v_cpu = wl.qkv(w, heads=H)             # [1, 32768, 32, 128] each
     qpos, kpos = wl.positions(w)
     q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    if args.inputs == "zeros":
+        for t in (q, k, v):
+            t.zero_()
     pos = torch.from_numpy(qpos).to(dev)
     share = ltxa.SpShare(max_tokens=32768, num_heads=H, head_dim=D, world_size=P)
     n_pad = share.set_seqlen(w.nq_valid)
@@ -284,7 +290,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic" if args.inputs == "normal" else "synthetic, all zeros (diagnostic, not a result)",
         "config": {"workload": WORKLOAD, "tokens": N, "valid_tokens": w.nq_valid, "heads": H,
                    "head_dim": D, "virtual_ranks": P, "heads_per_rank": Hl, "batch": B,
                    "grid_txy": list(w.q_grid), "rope_theta": w.theta, "path": args.path},
@@ -299,7 +305,7 @@ def main():
     }
     if args.secondary:
         line["secondary"] = secondary(ltxa, wl, dev, 20)
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.inputs == "normal":
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, qpos, kpos, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
