@@ -296,7 +296,7 @@ def main():
                    "grid_txy": list(w.q_grid), "rope_theta": w.theta, "path": args.path},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel<128>",
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, 8>",
                      "flop_per_launch": attn_flop, "avg_launch_ms": round(avg["attn_fwd"], 4)},
         "phases_ms": {k_: round(x, 4) for k_, x in avg.items()},
         "hbm_GBps": {**{k_: round(phase_bytes[k_] / (avg[k_] * 1e-3) / 1e9, 1)

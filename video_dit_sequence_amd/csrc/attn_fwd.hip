@@ -4,12 +4,16 @@
 // for its heads; padded keys are masked out).  bf16 inputs, bf16 matrix-core
 // products with fp32 accumulation, fp32 online softmax.
 //
-// Work split.  One workgroup = 8 waves = 256 query rows of one (batch, head);
-// each wave owns 32 query rows for the whole key loop.  Two waves share each
-// SIMD, so one wave's softmax (VALU) runs while the other's matrix
-// instructions execute.  Keys stream through LDS in tiles of 64 keys,
-// double-buffered: while tile i is consumed, tile i+1 is copied global ->
-// LDS directly (buffer_load ... lds, no register staging).
+// Work split.  One workgroup = W waves = 32 W query rows of one (batch,
+// head); each wave owns 32 query rows for the whole key loop.  Two waves
+// share each SIMD, so one wave's softmax (VALU) runs while the other's matrix
+// instructions execute: D = 128 uses 8-wave workgroups (255 registers per
+// lane: one workgroup per CU); D = 64 uses 4-wave workgroups, which need
+// fewer registers, so that several workgroups share a CU and overlap each
+// other's start and end (the D = 64 workloads have short key loops).  Keys
+// stream through LDS in tiles of 64 keys, double-buffered: while tile i is
+// consumed, tile i+1 is copied global -> LDS directly (buffer_load ... lds,
+// no register staging).
 //
 // Matrix-core orientation.  v_mfma_f32_32x32x16_bf16 computes a 32x32 fp32
 // tile C += A(32x16) * B(16x32).  Lane l supplies row (l % 32) of A and
@@ -68,10 +72,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;                // query rows per wave
-constexpr int kBQ = kWaves * kQW;      // query rows per workgroup
 constexpr int kBK = 64;                // keys per tile
 constexpr int kStages = 2;             // LDS ring depth
 constexpr float kSumGuard = 18446744073709551616.0f;  // 2^64: a lane's tile row sum above it raises m
@@ -139,12 +140,26 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_A
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Waves per workgroup for head dimension D, and the workgroups that must fit
+// on one CU at once (which bounds the registers per lane: 2 waves per SIMD
+// leave 256, 3 leave 168).
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+constexpr int waves_for() {
+  return D == 128 ? 8 : 4;
+}
+template <int W>
+constexpr int min_blocks_for() {
+  return W == 8 ? 1 : 3;
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
     int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
     int32_t out_heads) {
+  constexpr int kThreads = W * 64;
+  constexpr int kBQ = W * kQW;          // query rows per workgroup
   constexpr int KS = D / 16;            // 16-channel steps of K Q^T
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
   constexpr int CH = D / 8;             // 16-byte chunks per row
@@ -435,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   // ring is free once every wave has left the key loop), row-major with the
   // 16-byte chunks of row r permuted by XOR with r % CH, and writes whole
   // rows: 16 bytes per lane, 64 / CH rows per instruction.
-  static_assert(2 * kQW == kBK, "two waves' output tiles fill one ring stage");
+  static_assert(2 * kQW == kBK && W <= 8, "two waves' output tiles fill one ring stage");
   __syncthreads();
   char* const stage = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sV0 : sV1) + (wave & 1) * (kQW * ROW);
 #pragma unroll
@@ -466,11 +481,13 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
       int64_t(out_heads) != (batch / out_batch) * heads)
     return hipErrorInvalidValue;
   (void)hipGetLastError();  // report only this launch's error
+  constexpr int W = waves_for<D>();
+  constexpr int kBQ = W * kQW;
   const int64_t qblocks = (nq + kBQ - 1) / kBQ;
   const int64_t nblocks = qblocks * batch * heads;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(static_cast<uint32_t>(nblocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, W>), dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nq, nk_pad, nk_valid,
                      heads, static_cast<int32_t>(qblocks), static_cast<int32_t>(nblocks), scale_log2,
