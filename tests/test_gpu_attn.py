@@ -169,8 +169,9 @@ def test_attn_rejects_bad_arguments():
     assert L.ltxa_attn_fwd(p + 2, p, p, o.data_ptr(), None, 1, 2, 128, 64, 64, 64, 0.1, None) == ltxa.LTXA_E_ALIGN
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("pattern", ["rising", "steep", "falling", "wide"])
-def test_running_max_rescale_paths(pattern):
+def test_running_max_rescale_paths(pattern, D):
     # The kernel keeps the first tile's row max as its softmax offset m and
     # raises it only when a lane's tile sum of probabilities exceeds 2^64,
     # then rescales what it has accumulated and recomputes the tile.  Rising
@@ -178,10 +179,11 @@ def test_running_max_rescale_paths(pattern):
     # tripping the guard; steep norms (up to 40x) push them past 64 log2
     # units, so the guard fires, on many tiles; falling norms keep every
     # later score below m; a large scale spreads the scores so that most
-    # probabilities are tiny next to the largest ones.
-    print(f"attn rescale {pattern}", flush=True)
+    # probabilities are tiny next to the largest ones.  Both head dimensions
+    # run (they use different workgroup shapes).
+    print(f"attn rescale {pattern} D={D}", flush=True)
     g = torch.Generator().manual_seed({"rising": 11, "steep": 14, "falling": 12, "wide": 13}[pattern])
-    nq, nk, D = 300, 1000, 128
+    nq, nk = 300, 1000
     q = wl.randn_bf16((1, nq, 2, D), g)
     k = wl.randn_bf16((1, nk, 2, D), g).to(torch.float32)
     v = wl.randn_bf16((1, nk, 2, D), g)
@@ -205,7 +207,7 @@ def test_running_max_rescale_paths(pattern):
     # within twice the unit-variance bar, cosine at the bar.
     ref, _ = oracle.attention(f64(q), f64(k), f64(v), nkv, scale)
     e = attn_errors(got, ref)
-    print(f"rescale/{pattern}: {e}", flush=True)
+    print(f"rescale/{pattern}/D{D}: {e}", flush=True)
     assert np.all(np.isfinite(got))
     assert e["rel_rms"] <= 2 * ATTN_REL_RMS and e["cosine"] >= ATTN_COSINE, e
     # Against the oracle on the operands as the ABI documents the kernel
@@ -214,5 +216,5 @@ def test_running_max_rescale_paths(pattern):
     log2e = 1.4426950408889634
     q_r = bf16_round(f64(q) * scale * log2e) / log2e
     ref_r, lse_r = oracle.attention(q_r, f64(k), f64(v), nkv, 1.0)
-    assert_attn_close(got, ref_r, f"rescale/{pattern} (rounded q)")
+    assert_attn_close(got, ref_r, f"rescale/{pattern}/D{D} (rounded q)")
     assert np.max(np.abs(f64(L) - lse_r)) <= LSE_ABS
