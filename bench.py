@@ -121,15 +121,25 @@ def secondary(ltxa, wl, dev, iters):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
+        # These launches are short: run them back to back for ~100 ms first,
+        # so that the core clock has settled under the load (right after
+        # idle it starts lower), and time at least `iters` launches and 50 ms.
         a, b = ev(), ev()
+        fn()
         a.record(stream)
-        for _ in range(iters):
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        one = max(a.elapsed_time(b), 1e-3)
+        for _ in range(int(100.0 / one) + 3):
+            fn()
+        n = max(iters, int(50.0 / one))
+        a.record(stream)
+        for _ in range(n):
             fn()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters
+        return a.elapsed_time(b) / n
 
     w = wl.WORKLOADS["cross_24576x1000"]
     P, H = w.world_sizes[0], w.full_heads

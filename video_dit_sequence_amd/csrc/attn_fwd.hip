@@ -5,11 +5,11 @@
 // products with fp32 accumulation, fp32 online softmax.
 //
 // Work split.  One workgroup = W waves = 32 W query rows of one (batch,
-// head); each wave owns 32 query rows for the whole key loop.  Two waves
-// share each SIMD, so one wave's softmax (VALU) runs while the other's matrix
-// instructions execute: D = 128 uses 8-wave workgroups (255 registers per
-// lane: one workgroup per CU); D = 64 uses 4-wave workgroups, which need
-// fewer registers, so that several workgroups share a CU and overlap each
+// head); each wave owns 32 query rows for the whole key loop.  At least two
+// waves share each SIMD, so one wave's softmax (VALU) runs while another's
+// matrix instructions execute.  D = 128 uses 8-wave workgroups (255
+// registers per lane: one workgroup per CU, two waves per SIMD); D = 64 uses
+// 4-wave workgroups held to 168 registers, three per CU, which overlap each
 // other's start and end (the D = 64 workloads have short key loops).  Keys
 // stream through LDS in tiles of 64 keys, double-buffered: while tile i is
 // consumed, tile i+1 is copied global -> LDS directly (buffer_load ... lds,
