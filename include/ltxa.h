@@ -106,7 +106,10 @@ int ltxa_sp_unpack(const void* src, void* dst, int64_t batch, int64_t n_tokens,
  * (head_dim/2) mod A highest pairs are left as they are.  Pair (x0, x1) =
  * channels (2i, 2i+1) becomes (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos
  * phi).  Angles and products are computed in fp32 from fp64 per-pair
- * frequencies; results are rounded to bf16 (nearest even).
+ * frequencies; results are rounded to bf16 (nearest even).  When q and k
+ * are both given with the same q_pos pointer, token count, axis count and
+ * max_pos values (self-attention), one kernel rotates both and computes each
+ * angle once; the bits are those of two separate calls.
  * Errors: E_NULL (both q and k NULL, or a non-NULL tensor without its
  * positions or max_pos); E_SHAPE (batch, heads or a token count < 1, head_dim
  * odd or not in [2, 256], axes not in {1,2,3} or more axes than pairs,

@@ -49,6 +49,30 @@ def test_rope_matches_oracle(name):
         assert exact > 0.995, f"{name}/{key}: only {exact:.4f} equal the rounded exact value"
 
 
+@pytest.mark.parametrize("name,heads", [("tiny_231", 2), ("share_32768", 4)])
+def test_shared_positions_rotate_q_and_k_in_one_launch(name, heads):
+    # Q and K given with the same position buffer, token count and extents
+    # (self-attention) are rotated by one launch that computes each angle
+    # once: the bits must be those of two separate calls, and K must meet the
+    # oracle bar as Q does.
+    w = wl.WORKLOADS[name]
+    print(f"rope shared positions {name}", flush=True)
+    q, k, _ = wl.qkv(w, heads=heads)
+    qpos, _ = wl.positions(w)
+    pos = torch.from_numpy(qpos).to(DEV)
+    q1, k1 = q.to(DEV), k.to(DEV)
+    ltxa.rope_qk(q1, pos, w.q_max_pos, k1, pos, w.q_max_pos, w.theta)
+    q2, k2 = q.to(DEV), k.to(DEV)
+    ltxa.rope_qk(q2, pos, w.q_max_pos, None, None, None, w.theta)
+    ltxa.rope_qk(None, None, None, k2, pos, w.q_max_pos, w.theta)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(q1), bits(q2))
+    assert np.array_equal(bits(k1), bits(k2))
+    for got, x in ((q1, q), (k1, k)):
+        ok, exact = rope_ok(f64(got), oracle.rope_apply(f64(x), qpos, w.q_max_pos, w.theta), f64(x))
+        assert ok.all() and exact > 0.995
+
+
 @pytest.mark.parametrize("which", ["q", "k"])
 def test_rope_one_tensor_only(which):
     w = wl.WORKLOADS["tiny_231"]

@@ -39,11 +39,13 @@ hipError_t launch_perm(const void* src, void* dst, const PermPlan& plan, int wor
 
 // Rotary embedding of src [batch, n_tokens, heads, head_dim] into dst
 // [ranks, batch, n_tokens, heads/ranks, head_dim]; ranks = 1 with dst = src
-// rotates in place.
-hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
-                           int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                           const RopeMode& mode, const RopeTable& table, const RopeInner& inner,
-                           hipStream_t stream);
+// rotates in place.  A non-null src2 is a second tensor of the same shape
+// and positions, rotated into dst2 by the same launch, which computes the
+// angles once for both (shared grid only; the inner grid rejects it).
+hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
+                           const int32_t* pos, int64_t n_tokens, int32_t axes, int64_t batch, int32_t heads,
+                           int32_t head_dim, int32_t ranks, const RopeMode& mode, const RopeTable& table,
+                           const RopeInner& inner, hipStream_t stream);
 
 // Attention over [batch, nq, heads, head_dim] operands.  The output row of
 // (batch entry bb, token n, head h) is written at head slot

@@ -60,11 +60,22 @@ ltxa::RopeMode rope_mode(const ltxa_rope_opts* opts) {
 
 int rope_launch(const void* src, void* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
                 const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                double theta, const ltxa_rope_opts* opts, void* stream) {
+                double theta, const ltxa_rope_opts* opts, void* stream, void* second = nullptr) {
   return launch_status(ltxa::launch_rope_any(
-      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), pos, n_tokens, axes, batch, heads,
-      head_dim, ranks, rope_mode(opts), rope_table(head_dim, axes, max_pos, theta),
-      rope_inner(opts, head_dim, axes, max_pos, theta), static_cast<hipStream_t>(stream)));
+      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(second),
+      static_cast<uint16_t*>(second), pos, n_tokens, axes, batch, heads, head_dim, ranks, rope_mode(opts),
+      rope_table(head_dim, axes, max_pos, theta), rope_inner(opts, head_dim, axes, max_pos, theta),
+      static_cast<hipStream_t>(stream)));
+}
+
+// Q and K turn by the same angles when they share the position buffer, the
+// token count and the per-axis extents (self-attention).
+bool same_rotation(const int32_t* q_pos, int64_t nq, int32_t q_axes, const double* q_max_pos,
+                   const int32_t* k_pos, int64_t nk, int32_t k_axes, const double* k_max_pos) {
+  if (q_pos != k_pos || nq != nk || q_axes != k_axes) return false;
+  for (int a = 0; a < q_axes; ++a)
+    if (q_max_pos[a] != k_max_pos[a]) return false;
+  return true;
 }
 
 }  // namespace
@@ -114,6 +125,8 @@ LTXA_EXPORT int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t 
   const int rc = ltxa::check_rope(q, q_pos, nq, q_axes, q_max_pos, k, k_pos, nk, k_axes, k_max_pos,
                                   batch, heads, head_dim, theta);
   if (rc) return rc;
+  if (q && k && same_rotation(q_pos, nq, q_axes, q_max_pos, k_pos, nk, k_axes, k_max_pos))
+    return rope_launch(q, q, q_pos, nq, q_axes, q_max_pos, batch, heads, head_dim, 1, theta, nullptr, stream, k);
   if (q) {
     const int r = rope_launch(q, q, q_pos, nq, q_axes, q_max_pos, batch, heads, head_dim, 1, theta, nullptr,
                               stream);

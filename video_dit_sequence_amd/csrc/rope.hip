@@ -127,6 +127,7 @@ __device__ __forceinline__ void rotate_rows(const RowAddr* a, int count, int g, 
 
 template <bool SPLIT, bool F64>
 __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* src, uint16_t* dst,
+                                                               const uint16_t* src2, uint16_t* dst2,
                                                                const int32_t* __restrict__ pos,
                                                                int64_t n_tokens, int32_t axes, int64_t batch,
                                                                int32_t heads, int32_t head_dim, int32_t ranks,
@@ -148,16 +149,19 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
     if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
   }
 
+  // Rows of the first tensor, then (if given) the same rows of the second.
   const int32_t hl = heads / ranks;
   const int64_t rows = batch * heads;
-  for (int64_t r0 = 0; r0 < rows; r0 += kRowsInFlight) {
+  const int64_t all_rows = src2 ? 2 * rows : rows;
+  for (int64_t r0 = 0; r0 < all_rows; r0 += kRowsInFlight) {
     RowAddr a[kRowsInFlight];
-    const int count = rows - r0 < kRowsInFlight ? static_cast<int>(rows - r0) : kRowsInFlight;
+    const int count = all_rows - r0 < kRowsInFlight ? static_cast<int>(all_rows - r0) : kRowsInFlight;
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      const int64_t r = r0 + u;
+      const bool second = r0 + u >= rows;
+      const int64_t r = second ? r0 + u - rows : r0 + u;
       const int64_t b = r / heads, h = r - b * heads;
-      a[u] = row_addr(src, dst, b, n, h, n_tokens, heads, hl, batch, head_dim);
+      a[u] = row_addr(second ? src2 : src, second ? dst2 : dst, b, n, h, n_tokens, heads, hl, batch, head_dim);
     }
     rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
   }
@@ -215,17 +219,20 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
 }
 
 template <bool SPLIT, bool F64>
-hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
-                       int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, const RopeMode& mode,
-                       const RopeTable& table, const RopeInner& inner, hipStream_t stream) {
+hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
+                       const int32_t* pos, int64_t n_tokens, int32_t axes, int64_t batch, int32_t heads,
+                       int32_t head_dim, int32_t ranks, const RopeMode& mode, const RopeTable& table,
+                       const RopeInner& inner, hipStream_t stream) {
   constexpr int PPT = SPLIT ? 8 : 4;
   const int groups = head_dim / (2 * PPT);
   if (!mode.inner) {
     const int64_t blocks = (n_tokens * groups + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
-                       0, stream, src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode.mid, table);
+                       0, stream, src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim, ranks,
+                       mode.mid, table);
   } else {
+    if (src2) return hipErrorInvalidValue;
     const int64_t per_block = int64_t(kInnerTokensPerThread) * (kThreads / groups);
     const int64_t blocks = (n_tokens + per_block - 1) / per_block;
     if (blocks > 0x7fffffff || heads > 65535) return hipErrorInvalidConfiguration;
@@ -238,20 +245,20 @@ hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const int32_t* pos, i
 
 }  // namespace
 
-hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const int32_t* pos, int64_t n_tokens,
-                           int32_t axes, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                           const RopeMode& mode, const RopeTable& table, const RopeInner& inner,
-                           hipStream_t stream) {
+hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
+                           const int32_t* pos, int64_t n_tokens, int32_t axes, int64_t batch, int32_t heads,
+                           int32_t head_dim, int32_t ranks, const RopeMode& mode, const RopeTable& table,
+                           const RopeInner& inner, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's error
   if (mode.split)
-    return mode.f64 ? launch_mode<true, true>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
-                                              table, inner, stream)
-                    : launch_mode<true, false>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks,
-                                               mode, table, inner, stream);
-  return mode.f64 ? launch_mode<false, true>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
-                                             table, inner, stream)
-                  : launch_mode<false, false>(src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
-                                              table, inner, stream);
+    return mode.f64 ? launch_mode<true, true>(src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim,
+                                              ranks, mode, table, inner, stream)
+                    : launch_mode<true, false>(src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim,
+                                               ranks, mode, table, inner, stream);
+  return mode.f64 ? launch_mode<false, true>(src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim,
+                                             ranks, mode, table, inner, stream)
+                  : launch_mode<false, false>(src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim,
+                                              ranks, mode, table, inner, stream);
 }
 
 }  // namespace ltxa
