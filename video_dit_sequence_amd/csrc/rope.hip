@@ -149,22 +149,25 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
     if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
   }
 
-  // Rows of the first tensor, then (if given) the same rows of the second.
+  // Every (batch, head) row of the token, then (if given) the same rows of
+  // the second tensor.
   const int32_t hl = heads / ranks;
   const int64_t rows = batch * heads;
-  const int64_t all_rows = src2 ? 2 * rows : rows;
-  for (int64_t r0 = 0; r0 < all_rows; r0 += kRowsInFlight) {
-    RowAddr a[kRowsInFlight];
-    const int count = all_rows - r0 < kRowsInFlight ? static_cast<int>(all_rows - r0) : kRowsInFlight;
+  auto all_rows = [&](const uint16_t* from, uint16_t* to) __attribute__((always_inline)) {
+    for (int64_t r0 = 0; r0 < rows; r0 += kRowsInFlight) {
+      RowAddr a[kRowsInFlight];
+      const int count = rows - r0 < kRowsInFlight ? static_cast<int>(rows - r0) : kRowsInFlight;
 #pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) {
-      const bool second = r0 + u >= rows;
-      const int64_t r = second ? r0 + u - rows : r0 + u;
-      const int64_t b = r / heads, h = r - b * heads;
-      a[u] = row_addr(second ? src2 : src, second ? dst2 : dst, b, n, h, n_tokens, heads, hl, batch, head_dim);
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const int64_t r = r0 + u;
+        const int64_t b = r / heads, h = r - b * heads;
+        a[u] = row_addr(from, to, b, n, h, n_tokens, heads, hl, batch, head_dim);
+      }
+      rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
     }
-    rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
-  }
+  };
+  all_rows(src, dst);
+  if (src2) all_rows(src2, dst2);
 }
 
 template <bool SPLIT, bool F64>
