@@ -23,10 +23,13 @@
 //    stores are non-temporal: each byte is touched once.  (A mapping with
 //    whole token rows per wave, which reads 1 KiB per instruction, measured
 //    slower: it repeats the cos/sin for every head group.)
-//  * Inner grid (heads turn at different frequencies).  One thread owns one
-//    head and one pair group for a run of tokens: its frequencies are
-//    computed once (fp64 pow) and reused across the run of 4 tokens; the cos/sin are
-//    per token.  Lanes cover the groups of one head row, then tokens.
+//    With few tokens (a short text or audio sequence) the rows of a token
+//    are split over grid y, so that the launch still fills the chip.
+//  * Inner grid (heads turn at different frequencies).  A workgroup owns one
+//    head and a run of tokens; the head's frequencies are computed once per
+//    workgroup (one fp64 pow per pair, shared through LDS), and one thread
+//    owns one pair group of one token.  Lanes cover the groups of one head
+//    row, then tokens.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,7 +38,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsInFlight = 4;
-constexpr int kInnerTokensPerThread = 4;
+constexpr int kInnerTokensPerThread = 1;
+// Threads that keep every CU busy (256 CUs x 512): a shared-grid launch with
+// fewer (token, pair group) threads splits each token's rows over grid y.
+constexpr int64_t kFillThreads = 256 * 512;
 
 // cos/sin of the angle (pos + mid) * coef; fp32 or fp64 evaluation.
 template <bool F64>
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
                                                                const int32_t* __restrict__ pos,
                                                                int64_t n_tokens, int32_t axes, int64_t batch,
                                                                int32_t heads, int32_t head_dim, int32_t ranks,
-                                                               double mid, RopeTable table) {
+                                                               int32_t rows_per, double mid, RopeTable table) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
   const int groups = head_dim / (2 * PPT);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -149,12 +155,13 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
     if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
   }
 
-  // Every (batch, head) row of the token, then (if given) the same rows of
-  // the second tensor.
+  // This thread's chunk of the token's (batch, head) rows (grid y, rows_per
+  // rows each), then (if given) the same rows of the second tensor.
   const int32_t hl = heads / ranks;
-  const int64_t rows = batch * heads;
+  const int64_t first = static_cast<int64_t>(blockIdx.y) * rows_per;
+  const int64_t rows = batch * heads - first < rows_per ? batch * heads : first + rows_per;
   auto all_rows = [&](const uint16_t* from, uint16_t* to) __attribute__((always_inline)) {
-    for (int64_t r0 = 0; r0 < rows; r0 += kRowsInFlight) {
+    for (int64_t r0 = first; r0 < rows; r0 += kRowsInFlight) {
       RowAddr a[kRowsInFlight];
       const int count = rows - r0 < kRowsInFlight ? static_cast<int>(rows - r0) : kRowsInFlight;
 #pragma unroll
@@ -182,20 +189,28 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
   const int token_lanes = kThreads / lanes_per_token;
   const int g = threadIdx.x % groups;
   const int tl = threadIdx.x / groups;
-  if (tl >= token_lanes) return;
   const int32_t h = blockIdx.y;
 
-  // Frequencies of this thread's pairs: global pair gp of the grid's
-  // grid_heads * head_dim / 2 pairs; axis gp / n_ax, index gp % n_ax.
+  // Frequencies of the head's pairs, one fp64 pow per pair, shared through
+  // LDS: global pair gp of the grid's grid_heads * head_dim / 2 pairs has
+  // axis gp / n_ax and index gp % n_ax.
+  __shared__ double s_coef[128];
+  __shared__ int s_axis[128];
+  if (threadIdx.x < head_dim / 2) {
+    const int64_t gp = (static_cast<int64_t>(grid.head_offset) + h) * (head_dim / 2) + threadIdx.x;
+    const int64_t a = gp / grid.n_ax, k = gp - a * grid.n_ax;
+    s_axis[threadIdx.x] = a < axes ? static_cast<int>(a) : -1;
+    s_coef[threadIdx.x] =
+        a < axes ? pow(grid.theta, -static_cast<double>(k) / grid.n_ax) / grid.max_pos[a < axes ? a : 0] : 0.0;
+  }
+  __syncthreads();
+  if (tl >= token_lanes) return;
   double coef[PPT];
   int axis[PPT];
 #pragma unroll
   for (int e = 0; e < PPT; ++e) {
-    const int64_t gp = (static_cast<int64_t>(grid.head_offset) + h) * (head_dim / 2) + PPT * g + e;
-    const int64_t a = gp / grid.n_ax, k = gp - a * grid.n_ax;
-    axis[e] = a < axes ? static_cast<int>(a) : -1;
-    coef[e] = a < axes ? pow(grid.theta, -static_cast<double>(k) / grid.n_ax) / grid.max_pos[a < axes ? a : 0]
-                       : 0.0;
+    coef[e] = s_coef[PPT * g + e];
+    axis[e] = s_axis[PPT * g + e];
   }
 
   const int32_t hl = heads / ranks;
@@ -229,11 +244,24 @@ hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2,
   constexpr int PPT = SPLIT ? 8 : 4;
   const int groups = head_dim / (2 * PPT);
   if (!mode.inner) {
-    const int64_t blocks = (n_tokens * groups + kThreads - 1) / kThreads;
+    const int64_t threads = n_tokens * groups;
+    const int64_t blocks = (threads + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
-                       0, stream, src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim, ranks,
-                       mode.mid, table);
+    // Few tokens: split each token's rows over grid y so that the launch
+    // still fills the chip (each chunk recomputes its angles).
+    const int64_t rows = batch * heads;
+    int64_t chunks = (kFillThreads + threads - 1) / threads;
+    const int64_t max_chunks = (rows + kRowsInFlight - 1) / kRowsInFlight;
+    chunks = chunks < 1 ? 1 : chunks > max_chunks ? max_chunks : chunks;
+    chunks = chunks > 65535 ? 65535 : chunks;  // grid y limit
+    int64_t rows_per = (rows + chunks - 1) / chunks;
+    rows_per = (rows_per + kRowsInFlight - 1) / kRowsInFlight * kRowsInFlight;
+    chunks = (rows + rows_per - 1) / rows_per;
+    if (rows_per > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks),
+                       static_cast<uint32_t>(chunks)), dim3(kThreads), 0, stream, src, dst, src2, dst2, pos,
+                       n_tokens, axes, batch, heads, head_dim, ranks, static_cast<int32_t>(rows_per), mode.mid,
+                       table);
   } else {
     if (src2) return hipErrorInvalidValue;
     const int64_t per_block = int64_t(kInnerTokensPerThread) * (kThreads / groups);
