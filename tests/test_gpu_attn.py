@@ -66,6 +66,21 @@ def test_share_32768_sampled_rows():
     _compare(q, k, v, w.nk_valid, w.nq_valid, w.scale, rows=rows, what="share_32768")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_long_sequence_sampled_rows(D):
+    # Four times the longest workload sequence: 2048 full key tiles plus a
+    # ragged one, row sums over 131067 keys, query blocks far past 2^16
+    # rows.  Sampled rows against the oracle.
+    print(f"attn long sequence D={D}", flush=True)
+    g = torch.Generator().manual_seed(4242 + D)
+    n, nkv = 131072, 131072 - 5
+    q = wl.randn_bf16((1, n, 2, D), g)
+    k = wl.randn_bf16((1, n, 2, D), g)
+    v = wl.randn_bf16((1, n, 2, D), g)
+    rows = wl.sample_rows(n, 4242, n_head=16, n_tail=32, n_random=48)
+    _compare(q, k, v, nkv, n, 1.0 / np.sqrt(D), rows=rows, what=f"long_131072_D{D}")
+
+
 def test_cross_24576x1000_all_rows():
     w = wl.WORKLOADS["cross_24576x1000"]
     print("attn cross_24576x1000", flush=True)
