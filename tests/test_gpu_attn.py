@@ -81,6 +81,43 @@ def test_long_sequence_sampled_rows(D):
     _compare(q, k, v, nkv, n, 1.0 / np.sqrt(D), rows=rows, what=f"long_131072_D{D}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_degenerate_logits(D):
+    # Two limits with closed forms.  Q = 0: every valid key has weight
+    # 1/nk_valid, so each output row is the mean of the valid V rows and the
+    # LSE is log(nk_valid).  One dominant key per query, placed in a late
+    # tile with a logit ~136 while the others stay below ~50: its exponential
+    # overflows fp32 against the first tile's offset, the sum guard must catch
+    # that, and the output row is that key's V row.
+    print(f"attn degenerate logits D={D}", flush=True)
+    g = torch.Generator().manual_seed(77 + D)
+    nq, nk, nkv, H = 200, 1000, 997, 2
+    k = wl.randn_bf16((1, nk, H, D), g)
+    v = wl.randn_bf16((1, nk, H, D), g)
+    v[:, nkv:] = float("nan")                       # padding must never be read
+    q = torch.zeros((1, nq, H, D), dtype=torch.bfloat16)
+    o, L = _run(q, k, v, nkv, 1.0 / np.sqrt(D))
+    mean = f64(v)[:, :nkv].mean(axis=1)             # [1, H, D]
+    err = np.abs(f64(o) - mean[:, None])
+    assert err.max() <= 2 ** -8 * np.abs(mean).max() + 1e-6, err.max()
+    assert np.max(np.abs(f64(L) - np.log(nkv))) <= LSE_ABS
+
+    # Dominant keys: key 500 + i is alpha times query i (alpha = 12 at D = 128,
+    # 17 at D = 64), so query i's logit with it is ~136 while every other
+    # logit of that query stays below ~50.
+    qd = wl.randn_bf16((1, nq, H, D), g)
+    alpha = 12.0 if D == 128 else 17.0
+    kd = k.clone()
+    kd[:, 500:500 + nq] = (qd.to(torch.float32) * alpha).to(torch.bfloat16)
+    o, L = _run(qd, kd, v, nkv, 1.0 / np.sqrt(D))
+    got = f64(o)
+    ref, _ = oracle.attention(f64(qd), f64(kd), f64(v), nkv, 1.0 / np.sqrt(D))
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref)) <= 2e-2
+    want = f64(v)[0, 500:500 + nq]                  # [nq, H, D]: the dominant key's V row
+    assert np.max(np.abs(got[0] - want)) <= 2e-2
+
+
 def test_cross_24576x1000_all_rows():
     w = wl.WORKLOADS["cross_24576x1000"]
     print("attn cross_24576x1000", flush=True)
