@@ -85,3 +85,28 @@ def test_graph_capture_replays_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(bits(replayed), bits(st.out))
     assert not np.array_equal(bits(replayed), bits(eager))
+
+
+def test_concurrent_steps_on_two_streams():
+    # No state is shared between calls: two different steps in flight on two
+    # streams at once give the bits each gives alone.
+    print("streams: two steps on two streams", flush=True)
+    a = _Step("tiny_231", 4, 4)
+    b = _Step("full_6144", 32, 8)
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    ref_a, ref_b = a.out.clone(), b.out.clone()
+    a.out.zero_()
+    b.out.zero_()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            b.run()
+        with torch.cuda.stream(s2):
+            a.run()
+    s1.synchronize()
+    s2.synchronize()
+    assert np.array_equal(bits(a.out), bits(ref_a))
+    assert np.array_equal(bits(b.out), bits(ref_b))
