@@ -47,6 +47,9 @@ def parse():
                     help="also time the cross-attention and connector workloads (reported apart)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 skips it)")
+    ap.add_argument("--cpu-configs", type=float, default=0.0,
+                    help="also time the oracle on the other workloads (6144 tokens, 32761 of 32768, "
+                         "cross-attention) and its pack, this many CPU seconds each (0 skips it)")
     ap.add_argument("--inputs", choices=("normal", "zeros"), default="normal",
                     help="diagnostic only: 'zeros' runs the same step on all-zero Q/K/V, which "
                          "shows how far the chip's clock under matrix load depends on the data")
@@ -70,35 +73,50 @@ def traffic_per_launch():
     return t.get("hbm_bytes_per_launch")
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((i.get("num_threads", 1) for i in threadpool_info()), default=1))
+    except Exception:
+        return os.cpu_count()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, qpos, kpos, budget_s):
     """Time the oracle on a bounded sample: blocks of 256 query rows of
-    successive heads against all 32768 keys (rotary on the rows and keys,
+    successive heads against all valid keys (rotary on the rows and keys,
     then attention), until the time budget is spent."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     f64 = lambda t: t.to(torch.float64).numpy()
     rows_per_block = 256
     flops = 0.0
     done_rows = 0
     heads_used = 0
     t0 = time.perf_counter()
-    for h in range(w.full_heads):
+    for h in range(q.shape[2]):
         kh = f64(k[:, :, h:h + 1])
         vh = f64(v[:, :, h:h + 1])
         kr = oracle.rope_apply(kh, kpos, w.k_max_pos, w.theta)
         heads_used += 1
         for r0 in range(0, w.nq, rows_per_block):
-            rows = np.arange(r0, r0 + rows_per_block)
-            qr = oracle.rope_apply(f64(q[:, r0:r0 + rows_per_block, h:h + 1]), qpos[rows],
+            rows = np.arange(r0, min(r0 + rows_per_block, w.nq))
+            qr = oracle.rope_apply(f64(q[:, r0:r0 + len(rows), h:h + 1]), qpos[rows],
                                    w.q_max_pos, w.theta)
             oracle.attention(qr, kr, vh, w.nk_valid, w.scale)
-            flops += 4.0 * rows_per_block * w.nk_valid * w.head_dim
-            done_rows += rows_per_block
+            flops += 4.0 * len(rows) * w.nk_valid * w.head_dim
+            done_rows += len(rows)
             if time.perf_counter() - t0 >= budget_s:
                 break
         if time.perf_counter() - t0 >= budget_s:
@@ -108,6 +126,30 @@ def cpu_baseline(w, q, k, v, qpos, kpos, budget_s):
             "sample": f"{done_rows} query rows over {heads_used} head(s) x {w.nk_valid} keys, "
                       f"head_dim {w.head_dim}, fp64 numpy (rotary + attention), {dt:.1f} s",
             "host_cpus": os.cpu_count()}
+
+
+def cpu_oracle_configs(wl, budget_s):
+    """The oracle on the other workloads (same sampling as cpu_baseline) and
+    the oracle pack of one [1, 32768, 32, 128] bf16 tensor to 8 ranks."""
+    import numpy as np
+    import oracle
+    out = {"cpu_model": cpu_model(), "blas_threads": blas_threads(), "host_cpus": os.cpu_count()}
+    for name in ("full_6144", "ragged_32761", "cross_24576x1000"):
+        w = wl.WORKLOADS[name]
+        q, k, v = wl.qkv(w)
+        qpos, kpos = wl.positions(w)
+        r = cpu_baseline(w, q, k, v, qpos, kpos, budget_s)
+        out[name] = {"value": round(r["value"], 4), "unit": "TFLOP/s", "sample": r["sample"]}
+    w = wl.WORKLOADS[WORKLOAD]
+    x = wl.qkv(w, heads=w.full_heads)[0].view(torch.int16).numpy()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.sp_pack(x, w.world_sizes[0])
+        n += 1
+    dt = time.perf_counter() - t0
+    out["pack_share_32768_P8"] = {"value": round(2.0 * x.nbytes * n / dt / 1e9, 2), "unit": "GB/s",
+                                  "sample": f"{n} packs of {x.nbytes} bytes, numpy transpose copy, {dt:.1f} s"}
+    return out
 
 
 def secondary(ltxa, wl, dev, iters):
@@ -317,6 +359,8 @@ def main():
         line["secondary"] = secondary(ltxa, wl, dev, 20)
     if args.cpu_seconds > 0 and args.inputs == "normal":
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, qpos, kpos, args.cpu_seconds)
+    if args.cpu_configs > 0 and args.inputs == "normal":
+        line["cpu_oracle_configs"] = cpu_oracle_configs(wl, args.cpu_configs)
     print(json.dumps(line), flush=True)
 
 
