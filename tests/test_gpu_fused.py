@@ -30,6 +30,7 @@ PACK_ROPE_CASES = [
     ("cross_24576x1000", 32, 8, "q"),  # video queries, D=64
     ("cross_24576x1000", 32, 8, "k"),  # audio keys, 1 axis, ragged 1000 of 1024
     ("share_32768", 32, 8, "q"),       # the timed configuration, D=128
+    ("connector_1024", 32, 8, "k"),    # batch 2, 1-axis text positions, rows split over grid y
 ]
 
 
@@ -66,6 +67,7 @@ ATTN_UNPACK_CASES = [
     ("tiny_231", 6, 2),                # 3 heads per rank
     ("cross_24576x1000", 32, 8),
     ("full_6144", 32, 8),
+    ("connector_1024", 32, 8),         # batch 2: shard entry p * B + b lands in batch b
 ]
 
 
