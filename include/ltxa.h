@@ -139,10 +139,21 @@ int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
  *   nk_valid are never read, so their contents (NaN included) cannot reach
  *   the output.  Query rows past the caller's valid length are computed like
  *   any other row.
- * Arithmetic: q is multiplied by scale * log2(e) and rounded to bf16 once
- * (relative error <= 2^-9 per element, so logits move by at most 2^-9 of
- * sum_d |q_d k_d| * scale); then bf16 products with fp32 accumulation, fp32
- * online softmax in base 2, fp32 -> bf16 output rounding (nearest even).
+ * Arithmetic: q is multiplied by c = scale * log2(e) (both in fp32) and
+ * rounded to bf16 once: each element moves by at most 2^-8 of its value
+ * (bf16 keeps 8 significant bits), so the natural-log score s_ij moves by at
+ * most 2^-8 * scale * sum_d |q_id k_jd|.  Then exact bf16 products with fp32
+ * accumulation, a base-2 softmax in fp32 whose probabilities are rounded to
+ * bf16 (at most 2^-8 relative) both for the weighted sum of v and for the
+ * row sum, and fp32 -> bf16 output rounding (nearest even).  So, with
+ * delta_i = 2^-8 * scale * max_j sum_d |q_id k_jd| - ln(1 - 2^-8) plus
+ * fp32 accumulation terms: |lse_i - exact| <= delta_i, and every softmax
+ * weight is within a factor e^(+-2 delta_i) of the exact one.
+ * Inputs: Q and the K/V rows below nk_valid are expected to be finite.  A NaN
+ * or infinity there is not hidden: it makes non-finite every output row it
+ * reaches (its own row for a Q value; every row of the head for a K or V
+ * value).  The other rows keep the accuracy stated above; other heads are
+ * not affected at all.
  * Errors: E_NULL (q, k, v or o NULL); E_SHAPE (batch, heads, nq < 1;
  * head_dim not 64 or 128; nk_valid not in [1, nk_pad]; scale not finite and
  * > 0); E_ALIGN (a pointer not 16-byte aligned); E_ALIAS (o or lse overlaps

@@ -2,11 +2,15 @@
 SP page states (padded keys contribute nothing; head-sharded equals
 full-head), which the kernel meets bit-exactly by construction.
 
-Bar (bf16 outputs, unit-variance inputs, valid rows, all heads/channels):
-max-abs <= 2e-2 and mean-abs <= 2e-3; also relative RMS <= 1e-2 and cosine
->= 0.9999.  Large cases are compared on a row sample (first 128 rows, last
-256 valid rows, 512 seeded random rows per head): rows are independent, so
-each sampled row is an exact check.
+Bars, always against the plain fp64 oracle on the same bf16 inputs:
+* acceptance (bf16 outputs, unit-variance inputs, valid rows, all
+  heads/channels): max-abs <= 2e-2 and mean-abs <= 2e-3; also relative RMS
+  <= 1e-2 and cosine >= 0.9999;
+* error model (every case, LSE included): per-row and per-element bounds
+  derived from the kernel's documented arithmetic (parity.attn_error_bounds).
+Large cases are compared on a row sample (first 128 rows, last 256 valid
+rows, 512 seeded random rows per head): rows are independent, so each
+sampled row is an exact check.
 """
 
 import numpy as np
@@ -14,8 +18,7 @@ import pytest
 import torch
 
 import oracle
-from parity import (ATTN_COSINE, ATTN_REL_RMS, LSE_ABS, assert_attn_close, attn_errors, bf16_round, bits,
-                    f64)
+from parity import (assert_attn_close, assert_within_model, attn_errors, bits, f64, kernel_scaled_q)
 from video_dit_sequence_amd import ltxa
 from video_dit_sequence_amd import workloads as wl
 
@@ -36,11 +39,11 @@ def _compare(q, k, v, nk_valid, n_rows_valid, scale, rows=None, what=""):
     if rows is None:
         rows = np.arange(n_rows_valid)
     ref_o, ref_lse = oracle.attention(f64(q), f64(k), f64(v), nk_valid, scale, rows=rows)
-    got = f64(o)[:, rows]
+    got, got_lse = f64(o)[:, rows], f64(L)[:, :, rows]
     e = assert_attn_close(got, ref_o, what)
-    lse_err = np.max(np.abs(f64(L)[:, :, rows] - ref_lse))
-    assert lse_err <= LSE_ABS, f"{what}: lse error {lse_err}"
-    print(f"{what}: {e} lse_err={lse_err:.2e}", flush=True)
+    r_o, r_l = assert_within_model(got, got_lse, f64(q), f64(k), f64(v), nk_valid, scale, rows, what)
+    lse_err = np.max(np.abs(got_lse - ref_lse))
+    print(f"{what}: {e} lse_err={lse_err:.2e} model ratios o={r_o:.3f} lse={r_l:.3f}", flush=True)
     return o
 
 
@@ -100,7 +103,9 @@ def test_degenerate_logits(D):
     mean = f64(v)[:, :nkv].mean(axis=1)             # [1, H, D]
     err = np.abs(f64(o) - mean[:, None])
     assert err.max() <= 2 ** -8 * np.abs(mean).max() + 1e-6, err.max()
-    assert np.max(np.abs(f64(L) - np.log(nkv))) <= LSE_ABS
+    # Every probability is exp2(0) = 1 exactly and the fp32 row sum of ones is
+    # exact, so only the final log and its fp32 rounding remain.
+    assert np.max(np.abs(f64(L) - np.log(nkv))) <= 1e-5
 
     # Dominant keys: key 500 + i is alpha times query i (alpha = 12 at D = 128,
     # 17 at D = 64), so query i's logit with it is ~136 while every other
@@ -116,6 +121,32 @@ def test_degenerate_logits(D):
     assert np.max(np.abs(got - ref)) <= 2e-2
     want = f64(v)[0, 500:500 + nq]                  # [nq, H, D]: the dominant key's V row
     assert np.max(np.abs(got[0] - want)) <= 2e-2
+    assert_within_model(got, f64(L), f64(qd), f64(kd), f64(v), nkv, 1.0 / np.sqrt(D), what="dominant key")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_single_valid_key_many_rows(D):
+    # One valid key: every weight is 1, so each output row is that key's V
+    # row exactly (the first tile's max is the key's own score, exp2(0) = 1,
+    # the row sum is 1), and the LSE is the key's score, off only by the
+    # bf16 rounding of scale * log2(e) * q.  4096 rows x 2 heads give that
+    # rounding's error its full spread; the LSE must stay inside the model
+    # bound against the plain oracle.
+    print(f"attn single valid key D={D}", flush=True)
+    g = torch.Generator().manual_seed(31 + D)
+    nq, nk, H = 4096, 64, 2
+    q = wl.randn_bf16((1, nq, H, D), g)
+    k = wl.randn_bf16((1, nk, H, D), g)
+    v = wl.randn_bf16((1, nk, H, D), g)
+    k[:, 1:] = float("nan")
+    v[:, 1:] = float("nan")
+    o, L = _run(q, k, v, 1, 1.0 / np.sqrt(D))
+    assert np.array_equal(bits(o), np.broadcast_to(bits(v[:, :1]), o.shape))
+    r_o, r_l = assert_within_model(f64(o), f64(L), f64(q), f64(k[:, :1]), f64(v[:, :1]), 1, 1.0 / np.sqrt(D),
+                                   what=f"single key D{D}")
+    _, lse_ex = oracle.attention(f64(q), f64(k[:, :1]), f64(v[:, :1]), 1, 1.0 / np.sqrt(D))
+    err = np.abs(f64(L) - lse_ex)
+    print(f"single key D{D}: lse max err {err.max():.2e} mean {err.mean():.2e}, worst/bound {r_l:.3f}", flush=True)
 
 
 def test_cross_24576x1000_all_rows():
@@ -191,7 +222,7 @@ def test_head_share_equals_full_head_bit_exact():
     k = wl.randn_bf16((1, 4096, 32, 128), g).to(DEV)
     v = wl.randn_bf16((1, 4096, 32, 128), g).to(DEV)
     full = ltxa.attn_fwd(q, k, v, nk_valid=4000)
-    for P in (2, 8):
+    for P in (2, 4, 8):
         qs, ks, vs = (ltxa.sp_pack(x, P) for x in (q, k, v))
         Hl = 32 // P
         os_ = ltxa.attn_fwd(qs.view(P, 4096, Hl, 128), ks.view(P, 4096, Hl, 128),
@@ -253,20 +284,61 @@ def test_running_max_rescale_paths(pattern, D):
     nkv = nk - 3
     o, L = _run(q, k, v, nkv, scale)
     got = f64(o)
-    # Against the plain oracle: a sanity bound (the bars are defined for
-    # unit-variance logits; these reach ~100 log2 units, where the one bf16
-    # rounding of the scaled q alone moves logits by ~0.2): relative RMS
-    # within twice the unit-variance bar, cosine at the bar.
-    ref, _ = oracle.attention(f64(q), f64(k), f64(v), nkv, scale)
-    e = attn_errors(got, ref)
-    print(f"rescale/{pattern}/D{D}: {e}", flush=True)
     assert np.all(np.isfinite(got))
-    assert e["rel_rms"] <= 2 * ATTN_REL_RMS and e["cosine"] >= ATTN_COSINE, e
-    # Against the oracle on the operands as the ABI documents the kernel
-    # rounds them (scale * log2(e) * q rounded to bf16 once): the full bar,
-    # absolute bounds included, and the log-sum-exp bar.
-    log2e = 1.4426950408889634
-    q_r = bf16_round(f64(q) * scale * log2e) / log2e
-    ref_r, lse_r = oracle.attention(q_r, f64(k), f64(v), nkv, 1.0)
-    assert_attn_close(got, ref_r, f"rescale/{pattern}/D{D} (rounded q)")
-    assert np.max(np.abs(f64(L) - lse_r)) <= LSE_ABS
+    # Against the plain oracle: the error-model bounds.  At these logits
+    # (up to ~100 log2 units) the one bf16 rounding of scale * log2(e) * q
+    # moves a logit by up to 2^-8 of scale * sum_d |q_d k_d|, which is what
+    # the bounds allow; they are loose but derived, not tuned.
+    e = attn_errors(got, oracle.attention(f64(q), f64(k), f64(v), nkv, scale)[0])
+    r_o, r_l = assert_within_model(got, f64(L), f64(q), f64(k), f64(v), nkv, scale,
+                                   what=f"rescale/{pattern}/D{D}")
+    print(f"rescale/{pattern}/D{D}: vs plain oracle {e}, model ratios o={r_o:.3f} lse={r_l:.3f}", flush=True)
+    # The offset logic on its own: with q carrying the kernel's documented
+    # rounding, the rest of the arithmetic (fp32 scores, base-2 softmax with
+    # the raised offsets, bf16 probabilities) must meet the acceptance bar
+    # and the error model without the q term.
+    q_r = kernel_scaled_q(f64(q), scale)
+    ref_r, _ = oracle.attention(q_r, f64(k), f64(v), nkv, 1.0)
+    assert_attn_close(got, ref_r, f"rescale/{pattern}/D{D} (q as rounded by the kernel)")
+    assert_within_model(got, f64(L), q_r, f64(k), f64(v), nkv, 1.0, q_prerounded=True,
+                        what=f"rescale/{pattern}/D{D} (q as rounded by the kernel)")
+
+
+def test_nonfinite_valid_inputs_propagate():
+    # Non-finite values on valid rows are outside the contract's finite
+    # inputs, but they must not be hidden: a NaN in one query row makes that
+    # row's output and LSE NaN; a NaN in a valid key row, or an infinity in a
+    # valid value row, makes every output row of that head non-finite.  The
+    # other rows keep their accuracy: rows outside the NaN row's wave (32
+    # rows) are bit-identical, and rows inside it, whose wave takes the
+    # offset-raising path on every tile, still meet the bar.
+    print("attn non-finite valid inputs", flush=True)
+    for D in (128, 64):
+        g = torch.Generator().manual_seed(505 + D)
+        nq, nk, nkv, H = 300, 200, 190, 2
+        q = wl.randn_bf16((1, nq, H, D), g)
+        k = wl.randn_bf16((1, nk, H, D), g)
+        v = wl.randn_bf16((1, nk, H, D), g)
+        o0, l0 = _run(q, k, v, nkv, 1.0 / np.sqrt(D))
+        qn = q.clone()
+        qn[0, 77, 1, 5] = float("nan")
+        o1, l1 = _run(qn, k, v, nkv, 1.0 / np.sqrt(D))
+        b0, b1 = bits(o0), bits(o1)
+        assert np.all(np.isnan(f64(o1)[0, 77, 1])) and np.isnan(f64(l1)[0, 1, 77])
+        outside = np.ones(b0.shape, dtype=bool)
+        outside[0, 64:96, 1] = False                 # the wave of rows 64..95 of head 1
+        assert np.array_equal(b0[outside], b1[outside])
+        rows = np.array([r for r in range(64, 96) if r != 77])
+        ref, _ = oracle.attention(f64(q)[:, :, 1:], f64(k)[:, :, 1:], f64(v)[:, :, 1:], nkv, 1.0 / np.sqrt(D),
+                                  rows=rows)
+        assert_attn_close(f64(o1)[:, rows, 1:], ref, f"rows beside a NaN query row D{D}")
+        kn = k.clone()
+        kn[0, 150, 0, 3] = float("nan")
+        o2, _ = _run(q, kn, v, nkv, 1.0 / np.sqrt(D))
+        assert not np.any(np.isfinite(f64(o2)[0, :, 0]).all(axis=-1))
+        assert np.array_equal(bits(o2)[0, :, 1], b0[0, :, 1])
+        vn = v.clone()
+        vn[0, 3, 1, 9] = float("inf")
+        o3, _ = _run(q, k, vn, nkv, 1.0 / np.sqrt(D))
+        assert not np.any(np.isfinite(f64(o3)[0, :, 1]).all(axis=-1))
+        assert np.array_equal(bits(o3)[0, :, 0], b0[0, :, 0])

@@ -44,10 +44,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-file extra flags.  The attention kernel never reads a padded key, and
-# its scores come from finite bf16 products, so NaN-preserving max (which
-# costs an extra canonicalising instruction per element) is not needed.
-FILE_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"]}
+# Per-file extra flags (none at present).
+FILE_FLAGS = {}
 
 
 def _compile(src: str) -> str:

@@ -45,11 +45,14 @@
 // m is the first tile's row max and is not tracked per tile: the softmax is
 // invariant to the offset, and fp32/bf16 hold probabilities up to 2^127, so
 // m only has to rise when a probability could leave the safe range.  After
-// each tile's exponentials the lane's row sum is checked: above 2^64 (or not
-// finite), the tile's exact max becomes m, O and the sum are rescaled and
-// the tile's probabilities recomputed.  With the guard at 2^64, P <= 2^64,
-// O <= 2^64 * |v| * keys and the sum stay far inside fp32.  The row sum
-// adds the bf16-rounded probabilities that also feed the P*V product.
+// each tile's exponentials the lane's row sum is checked: at or above 2^64,
+// or not finite, the tile's exact max becomes m, O and the sum are rescaled
+// and the tile's probabilities recomputed.  With the guard at 2^64,
+// P <= 2^64, O <= 2^64 * |v| * keys and the sum stay far inside fp32.  The
+// row sum adds the bf16-rounded probabilities that also feed the P*V
+// product.  The guard tests the sum's bit pattern as an integer, so that a
+// NaN or infinite sum (from non-finite valid inputs) takes the same path on
+// any floating-point compile flags; such rows then come out non-finite.
 //
 // Output.  Staged per wave through LDS and stored as whole rows (see the
 // end of the kernel); the row addressing also lets the output land directly
@@ -75,7 +78,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kQW = 32;                // query rows per wave
 constexpr int kBK = 64;                // keys per tile
 constexpr int kStages = 2;             // LDS ring depth
-constexpr float kSumGuard = 18446744073709551616.0f;  // 2^64: a lane's tile row sum above it raises m
+constexpr uint32_t kSumGuardBits = 0x5f800000u;  // bits of 2^64: a lane's tile row sum at or above it raises m
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -377,10 +380,12 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     };
     probs();
     // m is only raised when a probability could leave the safe range (a
-    // lane's sum above kSumGuard, or not finite).  Then the tile's exact max
-    // becomes the new m, the accumulated state is rescaled and the
-    // probabilities are recomputed; P*V has not consumed them yet.
-    if (__builtin_amdgcn_ballot_w64(!(sum <= kSumGuard))) {
+    // lane's sum at or above 2^64, +inf or NaN: with the sign bit cleared,
+    // exactly the patterns that compare at or above kSumGuardBits as
+    // unsigned integers).  Then the tile's exact max becomes the new m, the
+    // accumulated state is rescaled and the probabilities are recomputed;
+    // P*V has not consumed them yet.
+    if (__builtin_amdgcn_ballot_w64((__builtin_bit_cast(uint32_t, sum) & 0x7fffffffu) >= kSumGuardBits)) {
       const float delta = fmaxf(tile_max(), 0.0f);
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       l *= alpha;
