@@ -257,10 +257,10 @@ def main():
     n_pad = share.set_seqlen(w.nq_valid)
     B, N, Hl = w.B, n_pad, H // P
 
-    # Preallocated per-rank buffers (the AttentionManager's receive buffers).
-    qs = torch.empty((P, B, N, Hl, D), dtype=torch.bfloat16, device=dev)
-    ks, vs, os_ = torch.empty_like(qs), torch.empty_like(qs), torch.empty_like(qs)
-    out = torch.empty_like(q)
+    # The share's own receive and output buffers (the AttentionManager's),
+    # allocated once here and reused by every step.
+    buf = share.buffers(B, dev)
+    qs, ks, vs, os_, out = buf["q"], buf["k"], buf["v"], buf["o_shards"], buf["out"]
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 

@@ -9,6 +9,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from video_dit_sequence_amd import ltxa
 
@@ -218,6 +219,35 @@ def test_sp_share_bookkeeping():
         ltxa.SpShare(max_tokens=232, num_heads=2, head_dim=64, world_size=4)
     t = ltxa.SpShare(max_tokens=231, num_heads=4, head_dim=64, world_size=4)
     assert t.tokens_per_rank_max == 58 and t.set_seqlen(231) == 232
+    with pytest.raises(TypeError):
+        ltxa.SpShare(max_tokens=64, num_heads=4, head_dim=64, world_size=2, tensor_dtype=torch.float32)
+
+
+def test_sp_share_owns_and_reuses_buffers():
+    # The page's AttentionManager owns the exchange buffers, sized for
+    # ceil(max_tokens / world_size) tokens per rank.  The sizing and reuse
+    # logic is host code; CPU tensors stand in for device memory here.
+    s = ltxa.SpShare(max_tokens=32761, num_heads=32, head_dim=128, world_size=8)
+    with pytest.raises(ValueError, match="set_seqlen"):
+        s.buffers(1, "cpu")
+    s.set_seqlen(32761)                       # 32768 after padding
+    b = s.buffers(1, "cpu")
+    assert b["q"].shape == (8, 1, 32768, 4, 128) and b["out"].shape == (1, 32768, 32, 128)
+    assert b["k"].shape == b["v"].shape == (8, 1, 32768, 4, 128)
+    cap = 4096 * 8 * 32 * 128                 # per-rank ceil(32761 / 8) = 4096 tokens x 8 ranks
+    assert all(s._store[n].numel() == cap for n in ("q", "k", "v", "out"))
+    ptrs = {n: t.data_ptr() for n, t in b.items()}
+    s.set_seqlen(6000)                        # a shorter step reuses the same memory
+    b2 = s.buffers(1, "cpu")
+    assert b2["q"].shape == (8, 1, 6000, 4, 128)
+    assert {n: t.data_ptr() for n, t in b2.items()} == ptrs
+    b3 = s.buffers(1, "cpu", nk=1024)         # cross-attention keys: a view of the same K/V buffers
+    assert b3["k"].shape == (8, 1, 1024, 4, 128) and b3["k"].data_ptr() == ptrs["k"]
+    b4 = s.buffers(2, "cpu")                  # batch 2 of 6000 tokens still fits
+    assert b4["q"].shape == (8, 2, 6000, 4, 128) and b4["q"].data_ptr() == ptrs["q"]
+    s.set_seqlen(32761)
+    b5 = s.buffers(2, "cpu")                  # batch 2 at max_tokens grows them once
+    assert b5["q"].shape == (8, 2, 32768, 4, 128) and s._store["q"].numel() == 2 * cap
 
 
 def test_binding_refuses_cpu_tensors():

@@ -102,7 +102,9 @@ def test_fused_and_unfused_paths_agree_bitwise():
     pg = torch.from_numpy(qpos).to(DEV)
     share = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     share.set_seqlen(w.nq_valid)
-    a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=True)
+    # The result is a view of the share's output buffer: copy it before the
+    # second call overwrites that buffer.
+    a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=True).clone()
     b = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=False)
     torch.cuda.synchronize()
     assert a.shape == b.shape == (1, w.nq_valid, 32, 128)

@@ -20,10 +20,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _path(q, k, v, qpos, kpos, q_max, k_max, n_valid, nk_valid, P, heads, D):
+def _path(q, k, v, qpos, kpos, q_max, k_max, n_valid, nk_valid, P, heads, D, self_attn=True):
+    """SpShare pads the sequence to its own length (a multiple of P); the
+    token-major inputs are cut to it (self-attention: K/V and their
+    positions too)."""
     share = ltxa.SpShare(max_tokens=32768, num_heads=heads, head_dim=D, world_size=P)
     n_pad = share.set_seqlen(n_valid)
-    assert n_pad == q.shape[1]
+    assert n_pad <= q.shape[1]
+    q, qpos = q[:, :n_pad].contiguous(), qpos[:n_pad]
+    if self_attn:
+        k, v, kpos = k[:, :n_pad].contiguous(), v[:, :n_pad].contiguous(), kpos[:n_pad]
     o = ltxa.sp_attention(q.to(DEV), k.to(DEV), v.to(DEV), share, torch.from_numpy(qpos).to(DEV), q_max,
                           torch.from_numpy(kpos).to(DEV), k_max, nk_valid=nk_valid)
     torch.cuda.synchronize()
@@ -63,17 +69,58 @@ def test_share_32768_bench_configuration():
     print(e, flush=True)
 
 
-def test_ragged_32761_eight_ranks():
+@pytest.mark.parametrize("P,n_pad", [(2, 32762), (4, 32764), (8, 32768)])
+def test_ragged_32761_ranks(P, n_pad):
+    # The SP page pads to the next multiple of world_size: 32762 tokens at
+    # P = 2, 32764 at P = 4, 32768 at P = 8 ("How the forward pass works",
+    # step 1).  Each runs the whole path through SpShare and is compared with
+    # the single-GPU oracle on sampled rows of all 32 heads.
     w = wl.WORKLOADS["ragged_32761"]
-    print("path ragged_32761 H=32 P=8", flush=True)
+    print(f"path ragged_32761 H=32 P={P}", flush=True)
     q, k, v = wl.qkv(w)
     qpos, kpos = wl.positions(w)
-    o = _path(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid, 8, 32, 128)
+    share = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=P)
+    assert share.set_seqlen(w.nq_valid) == n_pad
+    o = _path(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid, P, 32, 128)
     assert o.shape == (1, 32761, 32, 128)
-    rows = wl.sample_rows(w.nq_valid, w.seed, n_random=128)
+    rows = wl.sample_rows(w.nq_valid, w.seed + P, n_random=128)
     ref = _oracle_rows(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid,
                        w.theta, w.scale, rows)
-    assert_attn_close(f64(o)[:, rows], ref, "path ragged_32761")
+    e = assert_attn_close(f64(o)[:, rows], ref, f"path ragged_32761 P={P}")
+    print(e, flush=True)
+
+
+def test_share_buffers_reused_across_steps():
+    # Two steps of different lengths on one share run in the buffers the
+    # share allocated at its first step (AttentionManager owns them); the
+    # default result is a view of the owned output buffer, copy_out gives a
+    # tensor of its own.  Both steps match the oracle.
+    w = wl.WORKLOADS["tiny_231"]
+    print("path share buffer reuse", flush=True)
+    q, k, v = wl.qkv(w, heads=4)
+    qpos, kpos = wl.positions(w)
+    share = ltxa.SpShare(max_tokens=232, num_heads=4, head_dim=64, world_size=4)
+    ptrs = []
+    for n_valid in (231, 150):
+        n_pad = share.set_seqlen(n_valid)
+        pos = wl.video_positions(w.q_grid, 0, 231)[:n_valid]
+        pos = np.concatenate([pos, np.zeros((n_pad - n_valid, 3), np.int32)])
+        qd, kd, vd = (x[:, :n_pad].contiguous().to(DEV) for x in (q, k, v))
+        o = ltxa.sp_attention(qd, kd, vd, share, torch.from_numpy(pos).to(DEV), w.q_max_pos)
+        torch.cuda.synchronize()
+        ptrs.append((o.data_ptr(), share.buffers(1, DEV)["q"].data_ptr()))
+        ref = oracle.sp_path_single_gpu(f64(q)[:, :n_valid], f64(k)[:, :n_valid], f64(v)[:, :n_valid],
+                                        pos[:n_valid], pos[:n_valid], w.q_max_pos, w.k_max_pos, w.theta, w.scale)
+        assert_attn_close(f64(o), ref, f"reuse step n={n_valid}")
+    assert ptrs[0] == ptrs[1]
+    copy = ltxa.SpShare(max_tokens=232, num_heads=4, head_dim=64, world_size=4, copy_out=True)
+    copy.set_seqlen(231)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    c1 = ltxa.sp_attention(qd, kd, vd, copy, torch.from_numpy(qpos).to(DEV), w.q_max_pos)
+    c2 = ltxa.sp_attention(qd, kd, vd, copy, torch.from_numpy(qpos).to(DEV), w.q_max_pos)
+    torch.cuda.synchronize()
+    assert c1.data_ptr() != c2.data_ptr()
+    assert torch.equal(c1, c2)
 
 
 def test_cross_video_to_audio_eight_ranks():
@@ -81,7 +128,8 @@ def test_cross_video_to_audio_eight_ranks():
     print("path cross_24576x1000 H=32 P=8", flush=True)
     q, k, v = wl.qkv(w, heads=w.full_heads)
     qpos, kpos = wl.positions(w)
-    o = _path(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid, 8, 32, 64)
+    o = _path(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid, 8, 32, 64,
+              self_attn=False)
     rows = wl.sample_rows(w.nq_valid, w.seed, n_random=512)
     ref = _oracle_rows(q, k, v, qpos, kpos, w.q_max_pos, w.k_max_pos, w.nq_valid, w.nk_valid,
                        w.theta, w.scale, rows)

@@ -322,22 +322,43 @@ def attn_fwd_unpack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid:
 
 
 class SpShare:
-    """Bookkeeping of one SP attention group held as ``world_size`` virtual
-    ranks on one GPU (an ``AttentionManager`` analogue)."""
+    """Bookkeeping and exchange buffers of one SP attention group held as
+    ``world_size`` virtual ranks on one GPU (an ``AttentionManager`` analogue).
 
-    def __init__(self, max_tokens: int, num_heads: int, head_dim: int, world_size: int):
+    It checks ``num_heads % world_size``, pads each step's sequence to a
+    multiple of ``world_size`` (:meth:`set_seqlen`) and owns the per-rank
+    receive buffers: Q, K, V head shards ``[P, B, N_pad, H/P, D]`` and the
+    token-order output ``[B, N_pad, H, D]``.  They are allocated once, on
+    first use, for ``ceil(max_tokens / world_size)`` tokens per rank (K/V
+    buffers grow only if a call brings more keys, as cross-attention to a
+    longer sequence can), and every later step reuses them.
+
+    ``copy_out``: with ``False`` (the default) :func:`sp_attention` returns a
+    view of the owned output buffer, valid until the next call on this share;
+    with ``True`` it returns a tensor of its own.
+    """
+
+    _NAMES = ("q", "k", "v", "o_shards", "out")
+
+    def __init__(self, max_tokens: int, num_heads: int, head_dim: int, world_size: int,
+                 tensor_dtype: torch.dtype = torch.bfloat16, copy_out: bool = False):
         if max_tokens < 1 or num_heads < 1 or head_dim < 1 or world_size < 1:
             raise ValueError("max_tokens, num_heads, head_dim and world_size must be positive")
         if num_heads % world_size:
             raise ValueError(f"num_heads ({num_heads}) must be divisible by world_size ({world_size})")
+        if tensor_dtype != torch.bfloat16:
+            raise TypeError("the attention kernels take bfloat16 tensors")
         self.max_tokens = int(max_tokens)
         self.num_heads = int(num_heads)
         self.head_dim = int(head_dim)
         self.world_size = int(world_size)
+        self.tensor_dtype = tensor_dtype
+        self.copy_out = bool(copy_out)
         self.heads_per_rank = self.num_heads // self.world_size
         self.tokens_per_rank_max = -(-self.max_tokens // self.world_size)
         self.n_valid = 0
         self.n_pad = 0
+        self._store = {}      # name -> flat device tensor
 
     def set_seqlen(self, n_valid: int) -> int:
         """Record this step's token count; returns the padded length."""
@@ -354,6 +375,36 @@ class SpShare:
     def tokens_per_rank(self) -> int:
         return self.n_pad // self.world_size
 
+    def _view(self, name: str, shape, device) -> torch.Tensor:
+        numel = 1
+        for x in shape:
+            numel *= int(x)
+        buf = self._store.get(name)
+        if buf is None or buf.numel() < numel or buf.device != torch.device(device):
+            # First use: size for max_tokens (per rank ceil(max_tokens / P)
+            # tokens from each of P ranks) at this batch size, or the request
+            # if that is larger.
+            B = int(shape[1]) if name in ("q", "k", "v", "o_shards") else int(shape[0])
+            cap = B * self.tokens_per_rank_max * self.world_size * self.num_heads * self.head_dim
+            buf = torch.empty(max(numel, cap), dtype=self.tensor_dtype, device=device)
+            self._store[name] = buf
+        return buf[:numel].view(*shape)
+
+    def buffers(self, batch: int, device, nk: Optional[int] = None) -> dict:
+        """Views of the owned buffers for this step (:meth:`set_seqlen` first):
+        ``q``/``o_shards`` ``[P, B, n_pad, H/P, D]``, ``k``/``v``
+        ``[P, B, nk, H/P, D]`` (``nk`` defaults to ``n_pad``) and ``out``
+        ``[B, n_pad, H, D]``."""
+        if self.n_pad < 1:
+            raise ValueError("call set_seqlen before asking for buffers")
+        P, Hl, D, N = self.world_size, self.heads_per_rank, self.head_dim, self.n_pad
+        nk = N if nk is None else int(nk)
+        return {"q": self._view("q", (P, batch, N, Hl, D), device),
+                "k": self._view("k", (P, batch, nk, Hl, D), device),
+                "v": self._view("v", (P, batch, nk, Hl, D), device),
+                "o_shards": self._view("o_shards", (P, batch, N, Hl, D), device),
+                "out": self._view("out", (batch, N, self.num_heads, D), device)}
+
 
 def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpShare",
                  q_pos: torch.Tensor, q_max_pos, k_pos: Optional[torch.Tensor] = None,
@@ -364,10 +415,12 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     ``q``: token-major bf16 ``[B, N_pad, H, D]`` padded to ``share.n_pad``
     tokens; ``k``/``v``: ``[B, Nk_pad, H, D]`` (the same tensors' token count
     for self-attention).  Steps (SP page, "How the forward pass works"):
-    exchange heads (``ltxa_sp_pack``), rotate Q/K (``ltxa_rope_qk``), attend
-    over every valid key (``ltxa_attn_fwd``), shuffle back
-    (``ltxa_sp_unpack``) and drop padded rows (a view).  Returns
-    ``[B, share.n_valid, H, D]``.
+    exchange heads (``ltxa_sp_pack``) into the share's receive buffers,
+    rotate Q/K (``ltxa_rope_qk``), attend over every valid key
+    (``ltxa_attn_fwd``), shuffle back (``ltxa_sp_unpack``) into the share's
+    output buffer and drop padded rows (a view).  Returns
+    ``[B, share.n_valid, H, D]``: a view of the share's output buffer, or a
+    copy with ``share.copy_out``.
 
     With ``fused`` (the default) the same steps take four launches: Q and K
     are exchanged and rotated in one pass each (``ltxa_sp_pack_rope``), V is
@@ -383,19 +436,24 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     k_max_pos = q_max_pos if k_max_pos is None else k_max_pos
     nk_valid = share.n_valid if nk_valid is None else nk_valid
     Hl = H // P
+    buf = share.buffers(B, q.device, nk=Nk)
+    qs, ks, vs, out = buf["q"], buf["k"], buf["v"], buf["out"]
     if fused:
-        qs = sp_pack_rope(q, q_pos, q_max_pos, P, theta)
-        ks = sp_pack_rope(k, k_pos, k_max_pos, P, theta)
-        vs = sp_pack(v, P)
-        out = attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale)
-        return out[:, :share.n_valid]
-    qs = sp_pack(q, P).view(P * B, N, Hl, D)
-    ks = sp_pack(k, P).view(P * B, Nk, Hl, D)
-    vs = sp_pack(v, P).view(P * B, Nk, Hl, D)
-    rope_qk(qs, q_pos, q_max_pos, ks, k_pos, k_max_pos, theta)
-    os_ = attn_fwd(qs, ks, vs, nk_valid=nk_valid, scale=scale)
-    out = sp_unpack(os_.view(P, B, N, Hl, D))
-    return out[:, :share.n_valid]
+        sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs)
+        sp_pack_rope(k, k_pos, k_max_pos, P, theta, out=ks)
+        sp_pack(v, P, out=vs)
+        attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale, out=out)
+    else:
+        sp_pack(q, P, out=qs)
+        sp_pack(k, P, out=ks)
+        sp_pack(v, P, out=vs)
+        rope_qk(qs.view(P * B, N, Hl, D), q_pos, q_max_pos, ks.view(P * B, Nk, Hl, D), k_pos, k_max_pos, theta)
+        os_ = buf["o_shards"]
+        attn_fwd(qs.view(P * B, N, Hl, D), ks.view(P * B, Nk, Hl, D), vs.view(P * B, Nk, Hl, D),
+                 nk_valid=nk_valid, scale=scale, out=os_.view(P * B, N, Hl, D))
+        sp_unpack(os_, out=out)
+    res = out[:, :share.n_valid]
+    return res.clone() if share.copy_out else res
 
 
 def connector_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, max_pos,
