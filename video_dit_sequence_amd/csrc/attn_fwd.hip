@@ -116,13 +116,19 @@ __device__ __forceinline__ float partner(float x) {
 // distinct positions, and the 4 consecutive rows of a V transpose read
 // (which take 2 adjacent chunks each) land 4 positions apart.  Measured on
 // MI355X with SQ_LDS_BANK_CONFLICT: zero conflict cycles for both reads.
-// D = 64: 8 chunks per 128-byte row (two rows per 256-byte bank window).
+// D = 64: 8 chunks per 128-byte row, two rows per 256-byte bank window, so a
+// chunk's bank group is 8 (r & 1) + its position.  The permutation takes
+// each half (even rows, odd rows) of r..r+15 to 8 distinct positions (K
+// fragment reads), and gives rows r and r + 2 of a V transpose read
+// permutations that differ in bit 2, so that their chunks 0..3 (or 4..7)
+// fall in disjoint bank groups.  The earlier choice let those rows collide:
+// 1.34e7 conflict cycles per cross-attention launch, now 7.9e5.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128)
     return ((r & 3) << 2) | ((r >> 2) & 3);
   else
-    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    return ((r >> 2) & 3) | (((r >> 1) & 1) << 2);
 }
 
 // One 16-byte-per-lane copy global -> LDS through buffer resource r: lane l
@@ -360,8 +366,12 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     if (t == 0) shift(tile_max());   // the first tile sets m to its max
     float sum = 0.0f;
     bf16x8 pf[4];
+    // The lane's row sum runs as two chains of dot products, alternating by
+    // pair, and is added at the end: one chain of 16 dependent
+    // accumulations sat on the path to the sum guard and the P*V products
+    // (two chains: +2 % on the 32-head 32768-token launch).
     auto probs = [&] __device__() __attribute__((always_inline)) {
-      sum = 0.0f;
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         const int kb = G >> 1, j = G & 1;
@@ -372,11 +382,15 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
           bf16x2 pp;
           pp[0] = static_cast<__bf16>(p0);
           pp[1] = static_cast<__bf16>(p1);
-          sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+          if (e & 2)
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, s1, false);
+          else
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, s0, false);
           pf[G][e] = pp[0];
           pf[G][e + 1] = pp[1];
         }
       }
+      sum = s0 + s1;
     };
     probs();
     // m is only raised when a probability could leave the safe range (a
