@@ -156,19 +156,41 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
   }
 
   // This thread's chunk of the token's (batch, head) rows (grid y, rows_per
-  // rows each), then (if given) the same rows of the second tensor.
+  // rows each), then (if given) the same rows of the second tensor.  Rows go
+  // in (batch entry, head) order; a cursor keeps the source and destination
+  // row pointers and the (b, h, rank, head-in-rank) counters up to date with
+  // additions only (one divide per thread to place it at its first row).
   const int32_t hl = heads / ranks;
   const int64_t first = static_cast<int64_t>(blockIdx.y) * rows_per;
   const int64_t rows = batch * heads - first < rows_per ? batch * heads : first + rows_per;
+  const int64_t row_stride = int64_t(heads) * head_dim;         // token stride of the source
+  const int64_t rank_stride = batch * n_tokens * hl * head_dim;  // rank stride of the destination
   auto all_rows = [&](const uint16_t* from, uint16_t* to) __attribute__((always_inline)) {
+    int64_t b = first / heads;
+    int32_t h = static_cast<int32_t>(first - b * heads);
+    int32_t j = h % hl;
+    RowAddr cur = row_addr(from, to, b, n, h, n_tokens, heads, hl, batch, head_dim);
+    auto advance = [&]() __attribute__((always_inline)) {
+      cur.src += head_dim;
+      cur.dst += head_dim;
+      if (++j == hl) {  // next rank's shard, same batch entry and token
+        j = 0;
+        cur.dst += rank_stride - int64_t(hl) * head_dim;
+      }
+      if (++h == heads) {  // next batch entry, first head
+        h = 0;
+        ++b;
+        cur.src += (n_tokens - 1) * row_stride;
+        cur.dst = to + (b * n_tokens + n) * hl * head_dim;
+      }
+    };
     for (int64_t r0 = first; r0 < rows; r0 += kRowsInFlight) {
       RowAddr a[kRowsInFlight];
       const int count = rows - r0 < kRowsInFlight ? static_cast<int>(rows - r0) : kRowsInFlight;
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
-        const int64_t r = r0 + u;
-        const int64_t b = r / heads, h = r - b * heads;
-        a[u] = row_addr(from, to, b, n, h, n_tokens, heads, hl, batch, head_dim);
+        a[u] = cur;
+        if (u < count) advance();
       }
       rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
     }
