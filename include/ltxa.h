@@ -144,8 +144,9 @@ int ltxa_rope_qk(void* q, const int32_t* q_pos, int64_t nq, int32_t q_axes,
  * (bf16 keeps 8 significant bits), so the natural-log score s_ij moves by at
  * most 2^-8 * scale * sum_d |q_id k_jd|.  Then exact bf16 products with fp32
  * accumulation, a base-2 softmax in fp32 whose probabilities are rounded to
- * bf16 (at most 2^-8 relative) both for the weighted sum of v and for the
- * row sum, and fp32 -> bf16 output rounding (nearest even).  So, with
+ * bf16 (at most 2^-8 relative) for the weighted sum of v and summed
+ * unrounded in fp32 for the row sum, and fp32 -> bf16 output rounding
+ * (nearest even).  So, with
  * delta_i = 2^-8 * scale * max_j sum_d |q_id k_jd| - ln(1 - 2^-8) plus
  * fp32 accumulation terms: |lse_i - exact| <= delta_i, and every softmax
  * weight is within a factor e^(+-2 delta_i) of the exact one.

@@ -98,8 +98,10 @@ def attn_error_bounds(q: np.ndarray, k: np.ndarray, v: np.ndarray, nk_valid: int
         delta_i = scale * A_i * (U_BF16 (1 + 2^-14) + 2 D U_F32)   q rounded to bf16 once (c and
                                                                   the product in fp32), fp32
                                                                   accumulation of D products
-                  - ln(1 - U_BF16) + 4 U_F32                      each probability rounded to
-                                                                  bf16 after a fp32 exp2
+                  - ln(1 - U_BF16) + 4 U_F32                      fp32 exp2; the probabilities
+                                                                  weighting V rounded to bf16
+                                                                  (the row sum adds them
+                                                                  unrounded, which this covers)
     where A_i = max_j A_ij (``q_prerounded``: q already carries the
     kernel's rounding, so the first term drops to the accumulation part).
     Every weight w_j = p_j / sum p then moves by a factor in

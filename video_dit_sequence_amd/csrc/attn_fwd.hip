@@ -49,8 +49,8 @@
 // or not finite, the tile's exact max becomes m, O and the sum are rescaled
 // and the tile's probabilities recomputed.  With the guard at 2^64,
 // P <= 2^64, O <= 2^64 * |v| * keys and the sum stay far inside fp32.  The
-// row sum adds the bf16-rounded probabilities that also feed the P*V
-// product.  The guard tests the sum's bit pattern as an integer, so that a
+// probabilities feed the P*V product rounded to bf16; the row sum adds them
+// unrounded in fp32.  The guard tests the sum's bit pattern as an integer, so that a
 // NaN or infinite sum (from non-finite valid inputs) takes the same path on
 // any floating-point compile flags; such rows then come out non-finite.
 //
@@ -72,7 +72,6 @@ namespace ltxa {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kQW = 32;                // query rows per wave
@@ -301,7 +300,6 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   float m = 0.0f;       // replaced by the first tile's max
   float l = 0.0f;       // running sum over this lane's keys
   f32x16 neg_m = f32x16{};
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   auto compute_tile = [&] __device__(int t, const char* cK, const char* cV, auto masked)
                           __attribute__((always_inline)) {
@@ -366,10 +364,13 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     if (t == 0) shift(tile_max());   // the first tile sets m to its max
     float sum = 0.0f;
     bf16x8 pf[4];
-    // The lane's row sum runs as two chains of dot products, alternating by
-    // pair, and is added at the end: one chain of 16 dependent
-    // accumulations sat on the path to the sum guard and the P*V products
-    // (two chains: +2 % on the 32-head 32768-token launch).
+    // Probabilities: exp2 of the offset scores, rounded to bf16 for the P*V
+    // product.  The lane's row sum adds the unrounded fp32 values with plain
+    // adds, in two chains (even and odd keys) added at the end.  Measured on
+    // MI355X: v_dot2c_f32_bf16 (which would sum the bf16 values) does not
+    // overlap the matrix instructions while fp32 adds do; the adds are +2 %
+    // on the 32-head 32768-token launch over two dot-product chains, which
+    // were +2 % over one.
     auto probs = [&] __device__() __attribute__((always_inline)) {
       float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
@@ -379,15 +380,10 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
         for (int e = 0; e < 8; e += 2) {
           const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e]);
           const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e + 1]);
-          bf16x2 pp;
-          pp[0] = static_cast<__bf16>(p0);
-          pp[1] = static_cast<__bf16>(p1);
-          if (e & 2)
-            s1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, s1, false);
-          else
-            s0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, s0, false);
-          pf[G][e] = pp[0];
-          pf[G][e + 1] = pp[1];
+          pf[G][e] = static_cast<__bf16>(p0);
+          pf[G][e + 1] = static_cast<__bf16>(p1);
+          s0 += p0;
+          s1 += p1;
         }
       }
       sum = s0 + s1;
