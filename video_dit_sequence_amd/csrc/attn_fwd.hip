@@ -82,7 +82,7 @@ constexpr uint32_t kSumGuardBits = 0x5f800000u;  // bits of 2^64: a lane's tile 
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kKAhead = 3;        // K fragments in flight ahead of the products
-constexpr int kVAhead = 2;        // V fragments in flight ahead of the products
+constexpr int kVAhead = 3;        // V fragments in flight ahead of the products
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // chips: 32-bit data format, everything else zero.
 constexpr int kBufferFlags = 0x00020000;
