@@ -171,7 +171,12 @@ def test_ragged_32761_share_sampled_rows(P):
 
 @pytest.mark.parametrize("nq,nk_pad,nk_valid,D", [
     (1, 1, 1, 128), (1, 64, 1, 64), (129, 200, 65, 128), (300, 130, 129, 64),
-    (257, 64, 64, 128), (64, 4096, 4033, 128), (1000, 777, 700, 64)])
+    (257, 64, 64, 128), (64, 4096, 4033, 128), (1000, 777, 700, 64),
+    # The first tile runs outside the key loop, which then takes pairs of
+    # whole tiles: every way the tail can end (one or two tiles after the
+    # first, whole or masked, an odd or even number of whole tiles).
+    (100, 128, 128, 128), (100, 129, 129, 64), (100, 191, 191, 128), (100, 192, 192, 64),
+    (100, 193, 193, 128), (100, 256, 255, 64), (100, 320, 320, 128)])
 def test_ragged_shapes(nq, nk_pad, nk_valid, D):
     g = torch.Generator().manual_seed(nq * 7 + nk_valid)
     q = wl.randn_bf16((2, nq, 3, D), g)
