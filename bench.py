@@ -8,9 +8,12 @@ rank's share, so the rate equals one rank's.  Inputs are seeded synthetic
 bf16 N(0,1) tensors already resident in HBM.
 
 The default path takes four launches (``--path fused``): Q and K are packed
-and rotated in one pass each, V is packed, and the attention kernel writes
-its output in token order.  ``--path unfused`` times the six-launch sequence
-(pack x3, rotary, attention, unpack); both compute the same bits.
+and rotated in one pass each (the Q pass also multiplies by
+scale * log2(e) before its one rounding), V is packed, and the attention
+kernel takes those log2-domain queries as given and writes its output in
+token order.  ``--path unfused`` times the six-launch sequence (pack x3,
+rotary, attention, unpack), in which the attention kernel scales and
+rounds Q itself.
 
 Prints one JSON line.  ``value`` is attention TFLOP/s over the whole step
 (4 * Nq * Nk_valid * D * H flop per step).  ``roofline`` covers the dominant
@@ -191,14 +194,16 @@ def secondary(ltxa, wl, dev, iters):
     ks = torch.empty((P, w.B, w.nk_pad, H // P, w.head_dim), dtype=torch.bfloat16, device=dev)
     vs, o = torch.empty_like(ks), torch.empty_like(q)
 
+    c = ltxa.log2_domain_scale(w.scale)
+
     def cross():
-        ltxa.sp_pack_rope(q, qp, w.q_max_pos, P, w.theta, out=qs)
+        ltxa.sp_pack_rope(q, qp, w.q_max_pos, P, w.theta, out=qs, out_scale=c)
         ltxa.sp_pack_rope(k, kp, w.k_max_pos, P, w.theta, out=ks)
         ltxa.sp_pack(v, P, out=vs)
-        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o)
+        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o, q_log2=True)
 
     def cross_attn_only():
-        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o)
+        ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=o, q_log2=True)
 
     flop = 4.0 * w.nq * w.nk_valid * w.head_dim * H * w.B
     ms, ams = timed(cross), timed(cross_attn_only)
@@ -267,11 +272,13 @@ def main():
     if args.path == "fused":
         phase_names = ("pack_rope_qk", "pack_v", "attn_fwd")
 
+        c = ltxa.log2_domain_scale(w.scale)
+
         def launches():
-            ltxa.sp_pack_rope(q, pos, w.q_max_pos, P, w.theta, out=qs)
+            ltxa.sp_pack_rope(q, pos, w.q_max_pos, P, w.theta, out=qs, out_scale=c)
             yield ltxa.sp_pack_rope(k, pos, w.k_max_pos, P, w.theta, out=ks)
             yield ltxa.sp_pack(v, P, out=vs)
-            yield ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=out)
+            yield ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=out, q_log2=True)
     else:
         phase_names = ("pack_qkv", "rope_qk", "attn_fwd", "unpack_o")
 

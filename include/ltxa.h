@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 102 /* major*100 + minor */
+#define LTXA_VERSION 103 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -267,6 +267,51 @@ int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t
                          int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
                          int32_t head_dim, int32_t world_size, double theta,
                          const ltxa_rope_opts* opts, void* stream);
+
+/*
+ * Log2-domain queries.  The attention computes its softmax in base 2: with
+ * c = scale * log2(e), exp(scale * <q, k>) = 2^<c q, k>.  ltxa_attn_fwd
+ * multiplies q by c itself and rounds the product to bf16, on top of the
+ * rounding that produced q (the rotary embedding's, in the SP page's
+ * exchange of Q).  The two calls below move that multiplication into the
+ * rotary pack, ahead of its one rounding, so that each q value is rounded
+ * once in all.
+ */
+
+/*
+ * ltxa_sp_pack_rope_scaled -- ltxa_sp_pack_rope with every output value
+ * multiplied by out_scale before its rounding to bf16.  The rotation's cos
+ * and sin are multiplied by out_scale in fp32, once per token and pair, and
+ * then applied exactly as in ltxa_sp_pack_rope (channels a rotation leaves
+ * alone are multiplied by out_scale too).  With out_scale = 1, dst equals
+ * ltxa_sp_pack_rope's, bit for bit.  With out_scale = scale * log2(e), dst
+ * is the q operand of ltxa_attn_fwd_unpack_log2q.
+ * Errors: those of ltxa_sp_pack_rope; E_SHAPE (out_scale not finite and
+ * > 0).
+ */
+int ltxa_sp_pack_rope_scaled(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
+                             int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
+                             int32_t head_dim, int32_t world_size, double theta, float out_scale,
+                             void* stream);
+
+/*
+ * ltxa_attn_fwd_unpack_log2q -- ltxa_attn_fwd_unpack for queries already in
+ * the log2 domain (SP page, "What it is": each rank attends over all tokens
+ * for its heads).  q holds c * q_i for c = scale * log2(e), rounded to bf16
+ * (as ltxa_sp_pack_rope_scaled writes it), and is used as given: the scores
+ * are s_ij = ln(2) * <q_i, k_j>.  Layouts, masking, lse (natural log of the
+ * scores) and the rest of the arithmetic are those of ltxa_attn_fwd_unpack.
+ * The kernel neither multiplies nor rounds q again, so in ltxa_attn_fwd's
+ * bound the 2^-8 * scale * sum_d |q_id k_jd| term stands for the rounding
+ * of c * q itself: it is counted once, where ltxa_attn_fwd on a rounded q
+ * counts it twice.  With q = bf16(q' * c) formed in fp32, c being the
+ * double product scale * log2(e) rounded to fp32 (what ltxa_attn_fwd uses),
+ * o and lse equal ltxa_attn_fwd_unpack(q', scale) bit for bit.
+ * Errors: those of ltxa_attn_fwd_unpack (there is no scale to check).
+ */
+int ltxa_attn_fwd_unpack_log2q(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                               int64_t nk_pad, int64_t nk_valid, int32_t world_size, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -176,6 +176,14 @@ void pack_rope_checks() {
   EXPECT(check_pack_rope(dev(kA), dev(kB), devpos(kC), int64_t(1) << 42, 3, m, 1, 32, 128, 8, 1e4),
          LTXA_E_RANGE);
   EXPECT(check_pack_rope(dev(kA), dev(kA + 1024), devpos(kC), 32768, 3, m, 1, 32, 128, 8, 1e4), LTXA_E_ALIAS);
+  // Output scale of the scaled rotary pack.
+  EXPECT(ltxa::check_out_scale(0.12752f), LTXA_OK);
+  EXPECT(ltxa::check_out_scale(1.0f), LTXA_OK);
+  EXPECT(ltxa::check_out_scale(0.0f), LTXA_E_SHAPE);
+  EXPECT(ltxa::check_out_scale(-0.5f), LTXA_E_SHAPE);
+  EXPECT(ltxa::check_out_scale(std::numeric_limits<float>::infinity()), LTXA_E_SHAPE);
+  EXPECT(ltxa::check_out_scale(std::numeric_limits<float>::quiet_NaN()), LTXA_E_SHAPE);
+  EXPECT(ltxa::check_out_scale(std::numeric_limits<float>::denorm_min()), LTXA_OK);
 }
 
 void rope_opts_checks() {

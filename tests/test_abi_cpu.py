@@ -163,6 +163,43 @@ def test_attn_unpack_errors(L):
     assert f(A, B, C, D_, None, 1 << 40, 1 << 13, 128, 232, 232, 231, 0.1, 1 << 13, None) == ltxa.LTXA_E_RANGE
 
 
+def test_pack_rope_scaled_errors(L):
+    f = L.ltxa_sp_pack_rope_scaled
+    mp3 = _mp(3, 7, 11)
+    # as ltxa_sp_pack_rope, with out_scale before the stream
+    assert f(None, B, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, 232, 3, mp3, 0, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 231, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B + 8, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, A + 256, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_ALIAS
+    for bad in (0.0, -0.18, float("inf"), float("nan")):
+        assert f(A, B, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, bad, None) == ltxa.LTXA_E_SHAPE, bad
+
+
+def test_attn_unpack_log2q_errors(L):
+    f = L.ltxa_attn_fwd_unpack_log2q
+    good = (1, 8, 128, 232, 232, 231)  # no scale argument
+    assert f(None, B, C, D_, None, *good, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, None, None, *good, 2, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, D_, None, *good, 0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, *good, 3, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, C, D_, None, 1, 8, 96, 232, 232, 231, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 8, 128, 232, 232, 0, 2, None) == ltxa.LTXA_E_SHAPE
+    assert f(A + 8, B, C, D_, None, *good, 2, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, A + 64, None, *good, 2, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, D_, None, 1 << 40, 1 << 13, 128, 232, 232, 231, 1 << 13, None) == ltxa.LTXA_E_RANGE
+
+
+def test_log2_domain_scale_matches_kernel_rounding():
+    import numpy as np
+    for d in (64, 128):
+        sc = 1.0 / d ** 0.5
+        c = ltxa.log2_domain_scale(sc)
+        assert c == float(np.float32(c))                       # an fp32 value
+        assert abs(c - sc * 1.4426950408889634) <= 2 ** -24 * c  # the nearest one, to within rounding
+    assert ltxa.log2_domain_scale(1.0) == float(np.float32(1.4426950408889634))
+
+
 def _opts(**kw):
     return ctypes.byref(ltxa.rope_opts(**kw)) if kw else None
 

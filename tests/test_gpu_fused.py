@@ -8,6 +8,10 @@
 * ``ltxa_attn_fwd_unpack`` must equal, bit for bit, ``ltxa_attn_fwd`` over
   the shards followed by ``ltxa_sp_unpack`` (only the output addressing
   differs), with identical log-sum-exp values.
+* Log2-domain queries: ``ltxa_sp_pack_rope_scaled`` at scale 1 equals
+  ``ltxa_sp_pack_rope`` bit for bit, and at c = scale * log2(e) sits within
+  the rotary bar of c times the oracle's rotation; ``ltxa_attn_fwd_unpack_log2q``
+  on q' = bf16(q * c) equals ``ltxa_attn_fwd_unpack`` on q bit for bit.
 """
 
 import numpy as np
@@ -104,8 +108,98 @@ def test_fused_and_unfused_paths_agree_bitwise():
     share.set_seqlen(w.nq_valid)
     # The result is a view of the share's output buffer: copy it before the
     # second call overwrites that buffer.
-    a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=True).clone()
+    a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=True, prescale_q=False).clone()
     b = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, fused=False)
     torch.cuda.synchronize()
     assert a.shape == b.shape == (1, w.nq_valid, 32, 128)
     assert np.array_equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("name,heads,P,which", PACK_ROPE_CASES)
+def test_pack_rope_scaled(name, heads, P, which):
+    w = wl.WORKLOADS[name]
+    print(f"pack_rope_scaled {name} H={heads} P={P} {which}", flush=True)
+    q, k, _ = wl.qkv(w, heads=heads)
+    qpos, kpos = wl.positions(w)
+    x, pos, max_pos = (q, qpos, w.q_max_pos) if which == "q" else (k, kpos, w.k_max_pos)
+    xg, pg = x.to(DEV), torch.from_numpy(pos).to(DEV)
+    B, N, H, D = x.shape
+    plain = ltxa.sp_pack_rope(xg, pg, max_pos, P, w.theta)
+    one = ltxa.sp_pack_rope(xg, pg, max_pos, P, w.theta, out_scale=1.0)
+    c = ltxa.log2_domain_scale(w.scale)
+    scaled = ltxa.sp_pack_rope(xg, pg, max_pos, P, w.theta, out_scale=c)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(one), bits(plain))
+    if N * H * D <= 32 * 1024 * 1024:
+        x64 = f64(x)
+        ref = c * oracle.sp_pack(oracle.rope_apply(x64, pos, max_pos, w.theta), P)
+        ok, exact = rope_ok(f64(scaled), ref, c * oracle.sp_pack(x64, P))
+        assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
+        assert exact > 0.995
+
+
+@pytest.mark.parametrize("name,heads,P", ATTN_UNPACK_CASES)
+def test_attn_unpack_log2q_equals_kernel_scaled(name, heads, P):
+    w = wl.WORKLOADS[name]
+    print(f"attn_unpack_log2q {name} H={heads} P={P}", flush=True)
+    q, k, v = wl.qkv(w, heads=heads)
+    B, Nq, H, D = q.shape
+    Hl = H // P
+    qs, ks, vs = (ltxa.sp_pack(t.to(DEV), P) for t in (q, k, v))
+    c = ltxa.log2_domain_scale(w.scale)
+    q2 = (qs.float() * c).to(torch.bfloat16)   # the kernel's own fp32 product, rounded once
+    lse_a = torch.empty((P, B, Hl, Nq), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty_like(lse_a)
+    a = ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, scale=w.scale, lse=lse_a)
+    b = ltxa.attn_fwd_unpack(q2, ks, vs, nk_valid=w.nk_valid, lse=lse_b, q_log2=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(lse_a.view(-1).cpu().numpy().view(np.uint32),
+                          lse_b.view(-1).cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("name,heads,P,amp", [("tiny_231", 4, 4, 1), ("tiny_231", 4, 4, 8),
+                                              ("full_6144", 8, 8, 4)])
+def test_log2q_path_within_single_rounding_model(name, heads, P, amp):
+    """Q rotated and scaled by the rotary pack and used as given by the
+    attention: against the exact attention of the exactly rotated q (the
+    oracle's fp64 rope_apply) and of K as the kernel rotated it, the path
+    meets the error model with q rounded once (tests/parity.py).  amp
+    multiplies q by a power of two (exact in bf16) to make the logits steep,
+    where q's rounding is the largest term.  The unscaled path, where q is
+    rounded by the rotation and again by the attention kernel, is measured
+    beside it against the same exact result."""
+    from parity import assert_within_model, attn_error_bounds
+    w = wl.WORKLOADS[name]
+    print(f"log2q path {name} H={heads} P={P} amp={amp}", flush=True)
+    q, k, v = wl.qkv(w, heads=heads)
+    q = q * amp
+    qpos, _ = wl.positions(w)
+    B, N, H, D = q.shape
+    Hl = H // P
+    qg, kg, vg = (t.to(DEV) for t in (q, k, v))
+    pg = torch.from_numpy(qpos).to(DEV)
+    c = ltxa.log2_domain_scale(w.scale)
+    ks = ltxa.sp_pack_rope(kg, pg, w.q_max_pos, P, w.theta)
+    vs = ltxa.sp_pack(vg, P)
+    qs_l2 = ltxa.sp_pack_rope(qg, pg, w.q_max_pos, P, w.theta, out_scale=c)
+    qs = ltxa.sp_pack_rope(qg, pg, w.q_max_pos, P, w.theta)
+    lse_l2 = torch.empty((P, B, Hl, N), dtype=torch.float32, device=DEV)
+    lse_2r = torch.empty_like(lse_l2)
+    o_l2 = ltxa.attn_fwd_unpack(qs_l2, ks, vs, nk_valid=w.nk_valid, lse=lse_l2, q_log2=True)
+    o_2r = ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, scale=w.scale, lse=lse_2r)
+    k_rot = f64(ltxa.sp_unpack(ks))
+    torch.cuda.synchronize()
+
+    rows = (np.arange(w.nq_valid) if N <= 512 else wl.sample_rows(w.nq_valid, w.seed, n_random=192))
+    q_exact = oracle.rope_apply(f64(q), qpos, w.q_max_pos, w.theta)
+    to_bhn = lambda t: t.permute(1, 0, 2, 3).reshape(B, H, N).cpu().numpy().astype(np.float64)
+    r_o, r_l = assert_within_model(f64(o_l2)[:, rows], to_bhn(lse_l2)[:, :, rows], q_exact, k_rot, f64(v),
+                                   w.nk_valid, w.scale, rows=rows, what=f"log2q {name} amp={amp}")
+    lse_b, o_b, o_ex, lse_ex = attn_error_bounds(q_exact, k_rot, f64(v), w.nk_valid, w.scale, rows=rows)
+    r2_o = float(np.max(np.abs(f64(o_2r)[:, rows] - o_ex) / o_b))
+    r2_l = float(np.max(np.abs(to_bhn(lse_2r)[:, :, rows] - lse_ex) / lse_b))
+    e_l2 = float(np.max(np.abs(to_bhn(lse_l2)[:, :, rows] - lse_ex)))
+    e_2r = float(np.max(np.abs(to_bhn(lse_2r)[:, :, rows] - lse_ex)))
+    print(f"  worst error/bound (q rounded once): o {r_o:.3f} lse {r_l:.3f}; "
+          f"(q rounded twice): o {r2_o:.3f} lse {r2_l:.3f}; max |lse err| {e_l2:.2e} vs {e_2r:.2e}", flush=True)

@@ -39,7 +39,8 @@
 // one K fragment and the 4 rows read by one V transpose read fall in
 // different banks.
 //
-// Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once),
+// Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once;
+// or it arrives so multiplied, from the rotary pack, and is used as given),
 // so the products are log2-domain scores, and every score product starts
 // from a register block holding -m: exp2 consumes the accumulator as is.
 // m is the first tile's row max and is not tracked per tile: the softmax is
@@ -257,7 +258,8 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
   const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
   // Q is multiplied by scale * log2(e) once here (rounded back to bf16), so
-  // that the products are already log2-domain scores.
+  // that the products are already log2-domain scores.  (For log2-domain q
+  // the factor is 1.0f, and the value passes through unchanged.)
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch,
                     int32_t heads, int64_t nq, int64_t nk_pad, int64_t nk_valid, float scale,
-                    int64_t out_batch, int32_t out_heads, hipStream_t stream) {
+                    int64_t out_batch, int32_t out_heads, hipStream_t stream, bool q_log2) {
   if (out_batch < 1 || out_batch > batch || batch % out_batch != 0 ||
       int64_t(out_heads) != (batch / out_batch) * heads)
     return hipErrorInvalidValue;
@@ -508,7 +510,8 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   const int64_t qblocks = (nq + kBQ - 1) / kBQ;
   const int64_t nblocks = qblocks * batch * heads;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  // Log2-domain q is taken as given: x * 1.0f rounded to bf16 is x.
+  const float scale_log2 = q_log2 ? 1.0f : static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipLaunchKernelGGL((attn_fwd_kernel<D, W>), dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nq, nk_pad, nk_valid,
@@ -522,12 +525,12 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk_pad,
                        int64_t nk_valid, float scale, int64_t out_batch, int32_t out_heads,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool q_log2) {
   if (head_dim == 128)
     return launch_d<128>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, out_batch, out_heads,
-                         stream);
+                         stream, q_log2);
   return launch_d<64>(q, k, v, o, lse, batch, heads, nq, nk_pad, nk_valid, scale, out_batch, out_heads,
-                      stream);
+                      stream, q_log2);
 }
 
 }  // namespace ltxa

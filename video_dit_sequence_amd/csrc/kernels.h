@@ -32,6 +32,7 @@ struct RopeMode {
   bool inner;   // RopeInner grid instead of the shared RopeTable
   bool f64;     // angles and sin/cos in fp64
   double mid;   // 0, or 0.5 for cell-middle positions
+  float out_scale = 1.0f;  // every output value is the rotated value times this
 };
 
 hipError_t launch_perm(const void* src, void* dst, const PermPlan& plan, int world_size,
@@ -54,9 +55,11 @@ hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* s
 // out_batch = batch and out_heads = heads that is the operands' own layout;
 // with batch = P * out_batch and out_heads = P * heads it is the token-major
 // layout the per-rank shards came from.
+// q_log2: q already holds the log2-domain operands bf16(scale * log2(e) * q)
+// and is used as given (scale is then unused).
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk_pad,
                        int64_t nk_valid, float scale, int64_t out_batch, int32_t out_heads,
-                       hipStream_t stream);
+                       hipStream_t stream, bool q_log2 = false);
 
 }  // namespace ltxa

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
                                                                const int32_t* __restrict__ pos,
                                                                int64_t n_tokens, int32_t axes, int64_t batch,
                                                                int32_t heads, int32_t head_dim, int32_t ranks,
-                                                               int32_t rows_per, double mid, RopeTable table) {
+                                                               int32_t rows_per, double mid, float out_scale,
+                                                               RopeTable table) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
   const int groups = head_dim / (2 * PPT);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -153,6 +154,11 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
     c[e] = 1.0f;
     s[e] = 0.0f;
     if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
+    // An output scale turns (cos, sin) into (k cos, k sin) once per token:
+    // every row is then rotated and scaled with the same two fp32 operations
+    // per value and rounded to bf16 once.  k = 1 leaves both exact.
+    c[e] *= out_scale;
+    s[e] *= out_scale;
   }
 
   // This thread's chunk of the token's (batch, head) rows (grid y, rows_per
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
                                                               const int32_t* __restrict__ pos,
                                                               int64_t n_tokens, int32_t axes, int64_t batch,
                                                               int32_t heads, int32_t head_dim, int32_t ranks,
-                                                              double mid, RopeInner grid) {
+                                                              double mid, float out_scale, RopeInner grid) {
   constexpr int PPT = SPLIT ? 8 : 4;
   const int groups = head_dim / (2 * PPT);
   const int lanes_per_token = groups;
@@ -246,6 +252,8 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
       c[e] = 1.0f;
       s[e] = 0.0f;
       if (axis[e] >= 0) turn<F64>(pos[n * axes + axis[e]], mid, coef[e], c[e], s[e]);
+      c[e] *= out_scale;  // as in the shared-grid kernel
+      s[e] *= out_scale;
     }
     for (int64_t b0 = 0; b0 < batch; b0 += kRowsInFlight) {
       RowAddr a[kRowsInFlight];
@@ -283,7 +291,7 @@ hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2,
     hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks),
                        static_cast<uint32_t>(chunks)), dim3(kThreads), 0, stream, src, dst, src2, dst2, pos,
                        n_tokens, axes, batch, heads, head_dim, ranks, static_cast<int32_t>(rows_per), mode.mid,
-                       table);
+                       mode.out_scale, table);
   } else {
     if (src2) return hipErrorInvalidValue;
     const int64_t per_block = int64_t(kInnerTokensPerThread) * (kThreads / groups);
@@ -291,7 +299,7 @@ hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2,
     if (blocks > 0x7fffffff || heads > 65535) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((rope_inner_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks), heads),
                        dim3(kThreads), 0, stream, src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks,
-                       mode.mid, inner);
+                       mode.mid, mode.out_scale, inner);
   }
   return hipGetLastError();
 }

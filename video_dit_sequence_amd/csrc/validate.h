@@ -154,6 +154,11 @@ inline int check_pack_rope(const void* src, const void* dst, const int32_t* pos,
   return LTXA_OK;
 }
 
+// Output scale of the scaled rotary pack: finite and positive.
+inline int check_out_scale(float out_scale) {
+  return std::isfinite(out_scale) && out_scale > 0.0f ? LTXA_OK : LTXA_E_SHAPE;
+}
+
 // Attention over world_size head shards [world_size, batch, n, heads/world_size,
 // head_dim] with the output in the token-major [batch, nq, heads, head_dim]
 // layout: the same checks as check_attn over a batch of world_size * batch

@@ -19,6 +19,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,8 @@ LTXA_E_RANGE = -7
 
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
            "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
-           "ltxa_rope_ex", "ltxa_sp_pack_rope_ex")
+           "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_sp_pack_rope_scaled",
+           "ltxa_attn_fwd_unpack_log2q")
 
 LTXA_ROPE_INTERLEAVED = 0
 LTXA_ROPE_SPLIT = 1
@@ -107,6 +109,12 @@ def lib() -> ctypes.CDLL:
         L.ltxa_attn_fwd_unpack.restype = ctypes.c_int
         L.ltxa_attn_fwd_unpack.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                            ctypes.c_float, i32, vp]
+        L.ltxa_sp_pack_rope_scaled.restype = ctypes.c_int
+        L.ltxa_sp_pack_rope_scaled.argtypes = [vp, vp, vp, i64, i32, dp, i64, i32, i32, i32,
+                                               ctypes.c_double, ctypes.c_float, vp]
+        L.ltxa_attn_fwd_unpack_log2q.restype = ctypes.c_int
+        L.ltxa_attn_fwd_unpack_log2q.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
+                                                 i32, vp]
         _lib = L
     return _lib
 
@@ -251,14 +259,24 @@ def rope(x: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
         None if opts is None else ctypes.byref(opts), _stream_ptr(x)))
 
 
+def log2_domain_scale(scale: float) -> float:
+    """``scale * log2(e)`` as the attention kernel forms it: the fp32 scale
+    widened to double, multiplied, rounded to fp32.  Passed as ``out_scale``
+    to :func:`sp_pack_rope`, it makes the log2-domain queries that
+    :func:`attn_fwd_unpack` takes with ``q_log2=True``."""
+    return float(np.float32(np.float64(np.float32(scale)) * 1.4426950408889634))
+
+
 def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
                  theta: float = 10000.0, out: Optional[torch.Tensor] = None,
-                 opts: Optional[RopeOpts] = None) -> torch.Tensor:
+                 opts: Optional[RopeOpts] = None, out_scale: Optional[float] = None) -> torch.Tensor:
     """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` (``ltxa_sp_pack_rope``,
-    or ``ltxa_sp_pack_rope_ex`` when ``opts`` is given).
+    ``ltxa_sp_pack_rope_ex`` when ``opts`` is given, ``ltxa_sp_pack_rope_scaled``
+    when ``out_scale`` is).
 
     Equal, bit for bit, to :func:`sp_pack` followed by the rotation of each
-    rank's shard.  ``pos`` is an int32 ``[N, A]`` GPU tensor.
+    rank's shard.  ``pos`` is an int32 ``[N, A]`` GPU tensor.  ``out_scale``
+    multiplies every output value before its one rounding to bf16.
     """
     _gpu(src, "src", torch.bfloat16)
     _gpu(pos, "pos", torch.int32)
@@ -273,7 +291,13 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
     _gpu(out, "out", torch.bfloat16)
     if out.numel() != src.numel():
         raise ValueError("out has the wrong number of elements")
-    if opts is None:
+    if out_scale is not None:
+        if opts is not None:
+            raise ValueError("out_scale applies to the default rotation only (opts must be None)")
+        _check("ltxa_sp_pack_rope_scaled", lib().ltxa_sp_pack_rope_scaled(
+            src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
+            B, H, D, P, float(theta), float(out_scale), _stream_ptr(src)))
+    elif opts is None:
         _check("ltxa_sp_pack_rope", lib().ltxa_sp_pack_rope(
             src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
             B, H, D, P, float(theta), _stream_ptr(src)))
@@ -286,13 +310,15 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
 
 def attn_fwd_unpack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Optional[int] = None,
                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    lse: Optional[torch.Tensor] = None, q_log2: bool = False) -> torch.Tensor:
     """Attention over head shards ``[P, B, N, H/P, D]`` with the output in token
     order ``[B, Nq, H, D]`` (``ltxa_attn_fwd_unpack``).
 
     Equal, bit for bit, to :func:`attn_fwd` over the ``P * B`` shard entries
     followed by :func:`sp_unpack`.  ``lse``, if given, is float32
-    ``[P, B, H/P, Nq]``.
+    ``[P, B, H/P, Nq]``.  With ``q_log2`` the queries are already multiplied by
+    ``scale * log2(e)`` (:func:`log2_domain_scale`) and ``scale`` is not used
+    (``ltxa_attn_fwd_unpack_log2q``).
     """
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _gpu(t, name, torch.bfloat16)
@@ -315,9 +341,14 @@ def attn_fwd_unpack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid:
         if lse.shape != (P, B, Hl, Nq):
             raise ValueError("lse must be [P, B, H/P, Nq]")
         lse_ptr = lse.data_ptr()
-    _check("ltxa_attn_fwd_unpack", lib().ltxa_attn_fwd_unpack(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, P * Hl, D, Nq, Nk,
-        nk_valid, scale, P, _stream_ptr(q)))
+    if q_log2:
+        _check("ltxa_attn_fwd_unpack_log2q", lib().ltxa_attn_fwd_unpack_log2q(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, P * Hl, D, Nq, Nk,
+            nk_valid, P, _stream_ptr(q)))
+    else:
+        _check("ltxa_attn_fwd_unpack", lib().ltxa_attn_fwd_unpack(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, P * Hl, D, Nq, Nk,
+            nk_valid, scale, P, _stream_ptr(q)))
     return out
 
 
@@ -409,7 +440,7 @@ class SpShare:
 def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpShare",
                  q_pos: torch.Tensor, q_max_pos, k_pos: Optional[torch.Tensor] = None,
                  k_max_pos=None, nk_valid: Optional[int] = None, theta: float = 10000.0,
-                 scale: Optional[float] = None, fused: bool = True) -> torch.Tensor:
+                 scale: Optional[float] = None, fused: bool = True, prescale_q: bool = True) -> torch.Tensor:
     """One layer's SP attention for every virtual rank of ``share`` on one GPU.
 
     ``q``: token-major bf16 ``[B, N_pad, H, D]`` padded to ``share.n_pad``
@@ -425,7 +456,12 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     With ``fused`` (the default) the same steps take four launches: Q and K
     are exchanged and rotated in one pass each (``ltxa_sp_pack_rope``), V is
     exchanged, and attention writes token order directly
-    (``ltxa_attn_fwd_unpack``); the result is bit-identical.
+    (``ltxa_attn_fwd_unpack``).  With ``prescale_q`` (the default) the Q pass
+    also multiplies by ``scale * log2(e)`` before its one rounding
+    (``ltxa_sp_pack_rope_scaled``) and the attention takes those queries as
+    given (``ltxa_attn_fwd_unpack_log2q``): Q is rounded once instead of
+    twice.  With ``prescale_q=False`` the fused result is bit-identical to the
+    unfused one.
     """
     P = share.world_size
     B, N, H, D = q.shape
@@ -439,10 +475,14 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     buf = share.buffers(B, q.device, nk=Nk)
     qs, ks, vs, out = buf["q"], buf["k"], buf["v"], buf["out"]
     if fused:
-        sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs)
+        if prescale_q:
+            c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale))
+            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs, out_scale=c)
+        else:
+            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs)
         sp_pack_rope(k, k_pos, k_max_pos, P, theta, out=ks)
         sp_pack(v, P, out=vs)
-        attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale, out=out)
+        attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale, out=out, q_log2=prescale_q)
     else:
         sp_pack(q, P, out=qs)
         sp_pack(k, P, out=ks)
