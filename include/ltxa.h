@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 103 /* major*100 + minor */
+#define LTXA_VERSION 104 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -232,7 +232,13 @@ typedef struct ltxa_rope_opts {
   int32_t fp64_angles; /* 0: angle and sin/cos in fp32; 1: in fp64 (the
                           rotation itself stays fp32) */
   int32_t middle;      /* 0: angle uses pos; 1: pos + 1/2 (cell middles) */
-  int32_t reserved;    /* must be 0 */
+  float out_scale;     /* 0: none.  Otherwise finite and > 0: every output
+                          value is the rotated value times out_scale,
+                          rounded to bf16 once (cos and sin are multiplied
+                          by it in fp32, once per token and pair; channels
+                          the rotation leaves alone are scaled too).  With
+                          out_scale = scale * log2(e) the result is the q
+                          operand of the _log2q attention calls below. */
 } ltxa_rope_opts;
 
 /*
@@ -248,7 +254,8 @@ typedef struct ltxa_rope_opts {
  *   rotated one rank at a time (head_offset = rank * heads per rank), or
  *   through ltxa_sp_pack_rope_ex.
  * Errors: as ltxa_rope_qk for one tensor, plus E_NULL (pos or max_pos NULL),
- * E_SHAPE (rope_type, fp64_angles or middle not 0/1, reserved != 0,
+ * E_SHAPE (rope_type, fp64_angles or middle not 0/1, out_scale neither 0
+ * nor finite and > 0,
  * grid_heads < 0, head_offset < 0 or head_offset + heads > grid_heads, or
  * fewer grid pairs than axes), E_ALIGN (SPLIT with head_dim % 16 != 0).
  */
@@ -273,40 +280,38 @@ int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t
  * c = scale * log2(e), exp(scale * <q, k>) = 2^<c q, k>.  ltxa_attn_fwd
  * multiplies q by c itself and rounds the product to bf16, on top of the
  * rounding that produced q (the rotary embedding's, in the SP page's
- * exchange of Q).  The two calls below move that multiplication into the
- * rotary pack, ahead of its one rounding, so that each q value is rounded
- * once in all.
+ * exchange of Q).  The rotary calls with opts->out_scale = c make that
+ * product ahead of their one rounding, and the two calls below take such q
+ * as given, so that each q value is rounded once in all.
  */
 
 /*
- * ltxa_sp_pack_rope_scaled -- ltxa_sp_pack_rope with every output value
- * multiplied by out_scale before its rounding to bf16.  The rotation's cos
- * and sin are multiplied by out_scale in fp32, once per token and pair, and
- * then applied exactly as in ltxa_sp_pack_rope (channels a rotation leaves
- * alone are multiplied by out_scale too).  With out_scale = 1, dst equals
- * ltxa_sp_pack_rope's, bit for bit.  With out_scale = scale * log2(e), dst
- * is the q operand of ltxa_attn_fwd_unpack_log2q.
- * Errors: those of ltxa_sp_pack_rope; E_SHAPE (out_scale not finite and
- * > 0).
+ * ltxa_attn_fwd_log2q -- ltxa_attn_fwd for queries already in the log2
+ * domain (SP page, "What it is": attention stays global over all tokens).
+ * q holds c * q_i for c = scale * log2(e), rounded to bf16 (as
+ * ltxa_rope_ex / ltxa_sp_pack_rope_ex with opts->out_scale = c write it),
+ * and is used as given: the scores are s_ij = ln(2) * <q_i, k_j>.  Layouts,
+ * masking, lse (natural log of the scores) and the rest of the arithmetic
+ * are those of ltxa_attn_fwd.  The kernel neither multiplies nor rounds q
+ * again, so in ltxa_attn_fwd's bound the 2^-8 * scale * sum_d |q_id k_jd|
+ * term stands for the rounding of c * q itself: it is counted once, where
+ * ltxa_attn_fwd on a rounded q counts it twice.  With q = bf16(q' * c)
+ * formed in fp32, c being the double product scale * log2(e) rounded to
+ * fp32 (what ltxa_attn_fwd uses), o and lse equal ltxa_attn_fwd(q', scale)
+ * bit for bit.
+ * Errors: those of ltxa_attn_fwd (there is no scale to check).
  */
-int ltxa_sp_pack_rope_scaled(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
-                             int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
-                             int32_t head_dim, int32_t world_size, double theta, float out_scale,
-                             void* stream);
+int ltxa_attn_fwd_log2q(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                        int64_t nk_pad, int64_t nk_valid, void* stream);
 
 /*
- * ltxa_attn_fwd_unpack_log2q -- ltxa_attn_fwd_unpack for queries already in
- * the log2 domain (SP page, "What it is": each rank attends over all tokens
- * for its heads).  q holds c * q_i for c = scale * log2(e), rounded to bf16
- * (as ltxa_sp_pack_rope_scaled writes it), and is used as given: the scores
- * are s_ij = ln(2) * <q_i, k_j>.  Layouts, masking, lse (natural log of the
- * scores) and the rest of the arithmetic are those of ltxa_attn_fwd_unpack.
- * The kernel neither multiplies nor rounds q again, so in ltxa_attn_fwd's
- * bound the 2^-8 * scale * sum_d |q_id k_jd| term stands for the rounding
- * of c * q itself: it is counted once, where ltxa_attn_fwd on a rounded q
- * counts it twice.  With q = bf16(q' * c) formed in fp32, c being the
- * double product scale * log2(e) rounded to fp32 (what ltxa_attn_fwd uses),
- * o and lse equal ltxa_attn_fwd_unpack(q', scale) bit for bit.
+ * ltxa_attn_fwd_unpack_log2q -- ltxa_attn_fwd_unpack for log2-domain
+ * queries: the q operand, arithmetic and bit-exactness statement of
+ * ltxa_attn_fwd_log2q, the layouts of ltxa_attn_fwd_unpack (q as
+ * ltxa_sp_pack_rope_ex with opts->out_scale = c writes it).  o and lse equal
+ * ltxa_attn_fwd_log2q over the world_size * batch shard entries followed by
+ * ltxa_sp_unpack, bit for bit.
  * Errors: those of ltxa_attn_fwd_unpack (there is no scale to check).
  */
 int ltxa_attn_fwd_unpack_log2q(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -190,8 +190,8 @@ void rope_opts_checks() {
   using ltxa::check_rope_ex;
   std::vector<double> mp1 = {1024.0};
   const double* m = mp1.data();
-  auto opts = [](int32_t type, int32_t grid, int32_t off, int32_t f64, int32_t mid, int32_t res) {
-    ltxa_rope_opts* o = new ltxa_rope_opts{type, grid, off, f64, mid, res};
+  auto opts = [](int32_t type, int32_t grid, int32_t off, int32_t f64, int32_t mid, float scale) {
+    ltxa_rope_opts* o = new ltxa_rope_opts{type, grid, off, f64, mid, scale};
     return o;
   };
   auto run = [&](const ltxa_rope_opts* o, int32_t heads = 32, int32_t hd = 128) {
@@ -206,7 +206,10 @@ void rope_opts_checks() {
   EXPECT(run(opts(2, 0, 0, 0, 0, 0)), LTXA_E_SHAPE);
   EXPECT(run(opts(0, 0, 0, 2, 0, 0)), LTXA_E_SHAPE);
   EXPECT(run(opts(0, 0, 0, 0, 2, 0)), LTXA_E_SHAPE);
-  EXPECT(run(opts(0, 0, 0, 0, 0, 1)), LTXA_E_SHAPE);
+  EXPECT(run(opts(0, 0, 0, 0, 0, 0.18033688f)), LTXA_OK);   // out_scale = log2(e) / 8
+  EXPECT(run(opts(0, 0, 0, 0, 0, -1.0f)), LTXA_E_SHAPE);
+  EXPECT(run(opts(0, 0, 0, 0, 0, std::numeric_limits<float>::infinity())), LTXA_E_SHAPE);
+  EXPECT(run(opts(0, 0, 0, 0, 0, std::numeric_limits<float>::quiet_NaN())), LTXA_E_SHAPE);
   EXPECT(run(opts(0, -1, 0, 0, 0, 0)), LTXA_E_SHAPE);
   EXPECT(run(opts(0, 32, -1, 0, 0, 0)), LTXA_E_SHAPE);
   EXPECT(run(opts(0, 31, 0, 0, 0, 0)), LTXA_E_SHAPE);        // 32 heads do not fit in 31

@@ -163,17 +163,27 @@ def test_attn_unpack_errors(L):
     assert f(A, B, C, D_, None, 1 << 40, 1 << 13, 128, 232, 232, 231, 0.1, 1 << 13, None) == ltxa.LTXA_E_RANGE
 
 
-def test_pack_rope_scaled_errors(L):
-    f = L.ltxa_sp_pack_rope_scaled
-    mp3 = _mp(3, 7, 11)
-    # as ltxa_sp_pack_rope, with out_scale before the stream
-    assert f(None, B, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_NULL
-    assert f(A, B, C, 232, 3, mp3, 0, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_SHAPE
-    assert f(A, B, C, 231, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_DIVISIBILITY
-    assert f(A, B + 8, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_ALIGN
-    assert f(A, A + 256, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, 0.18, None) == ltxa.LTXA_E_ALIAS
-    for bad in (0.0, -0.18, float("inf"), float("nan")):
-        assert f(A, B, C, 232, 3, mp3, 1, 4, 64, 2, 1e4, bad, None) == ltxa.LTXA_E_SHAPE, bad
+def test_rope_opts_out_scale_layout():
+    # out_scale took the place of a reserved int32 that had to be 0: the
+    # struct keeps its size and offsets, and 0 still means "as before".
+    assert ctypes.sizeof(ltxa.RopeOpts) == 6 * 4
+    assert ltxa.RopeOpts.out_scale.offset == 5 * 4
+    text = open(HEADER).read()
+    assert re.search(r"float out_scale;", text) and "reserved" not in text
+    o = ltxa.rope_opts()
+    assert o.out_scale == 0.0
+
+
+def test_attn_log2q_errors(L):
+    f = L.ltxa_attn_fwd_log2q
+    good = (1, 8, 128, 232, 232, 231)  # no scale argument
+    assert f(None, B, C, D_, None, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, None, None, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, D_, None, 0, 8, 128, 232, 232, 231, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 8, 96, 232, 232, 231, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, D_, None, 1, 8, 128, 232, 232, 0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A + 8, B, C, D_, None, *good, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, A + 64, None, *good, None) == ltxa.LTXA_E_ALIAS
 
 
 def test_attn_unpack_log2q_errors(L):
@@ -218,7 +228,8 @@ def test_rope_ex_errors(L):
     assert f(A, C, 232, 3, mp3, 0, 4, 64, 1e4, None, None) == ltxa.LTXA_E_SHAPE
     assert f(A, C, 232, 3, mp3, 1, 4, 62, 1e4, None, None) == ltxa.LTXA_E_ALIGN
     assert f(A + 2, C, 232, 3, mp3, 1, 4, 64, 1e4, None, None) == ltxa.LTXA_E_ALIGN
-    bad = [(2, 0, 0, 0, 0, 0), (0, 0, 0, 2, 0, 0), (0, 0, 0, 0, 2, 0), (0, 0, 0, 0, 0, 1),
+    bad = [(2, 0, 0, 0, 0, 0), (0, 0, 0, 2, 0, 0), (0, 0, 0, 0, 2, 0), (0, 0, 0, 0, 0, -1.0),
+           (0, 0, 0, 0, 0, float("inf")), (0, 0, 0, 0, 0, float("nan")),
            (0, -1, 0, 0, 0, 0), (0, 4, -1, 0, 0, 0), (0, 4, 1, 0, 0, 0), (0, 3, 0, 0, 0, 0)]
     for vals in bad:
         assert f(A, C, 232, 3, mp3, 1, 4, 64, 1e4, _raw_opts(*vals), None) == ltxa.LTXA_E_SHAPE, vals
@@ -238,7 +249,7 @@ def test_pack_rope_ex_errors(L):
     assert f(A, A + 256, C, *args, None, None) == ltxa.LTXA_E_ALIAS
     assert f(A, B, C, *args, _opts(grid_heads=3), None) == ltxa.LTXA_E_SHAPE     # 4 heads > 3
     assert f(A, B, C, *args, _opts(grid_heads=5, head_offset=2), None) == ltxa.LTXA_E_SHAPE
-    assert f(A, B, C, *args, _raw_opts(0, 0, 0, 0, 0, 7), None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, *args, _raw_opts(0, 0, 0, 0, 0, -7.0), None) == ltxa.LTXA_E_SHAPE
     assert f(A, B, C, 232, 3, mp3, 1, 4, 40, 2, 1e4, _opts(rope_type="split"), None) == ltxa.LTXA_E_ALIGN
 
 

@@ -8,10 +8,12 @@
 * ``ltxa_attn_fwd_unpack`` must equal, bit for bit, ``ltxa_attn_fwd`` over
   the shards followed by ``ltxa_sp_unpack`` (only the output addressing
   differs), with identical log-sum-exp values.
-* Log2-domain queries: ``ltxa_sp_pack_rope_scaled`` at scale 1 equals
-  ``ltxa_sp_pack_rope`` bit for bit, and at c = scale * log2(e) sits within
-  the rotary bar of c times the oracle's rotation; ``ltxa_attn_fwd_unpack_log2q``
-  on q' = bf16(q * c) equals ``ltxa_attn_fwd_unpack`` on q bit for bit.
+* Log2-domain queries: ``ltxa_sp_pack_rope_ex`` with ``opts->out_scale`` = 1
+  equals ``ltxa_sp_pack_rope`` bit for bit, and with c = scale * log2(e)
+  sits within the rotary bar of c times the oracle's rotation (so does the
+  in-place ``ltxa_rope_ex``); ``ltxa_attn_fwd_unpack_log2q`` and
+  ``ltxa_attn_fwd_log2q`` on q' = bf16(q * c) equal ``ltxa_attn_fwd_unpack``
+  and ``ltxa_attn_fwd`` on q bit for bit.
 """
 
 import numpy as np
@@ -203,3 +205,46 @@ def test_log2q_path_within_single_rounding_model(name, heads, P, amp):
     e_2r = float(np.max(np.abs(to_bhn(lse_2r)[:, :, rows] - lse_ex)))
     print(f"  worst error/bound (q rounded once): o {r_o:.3f} lse {r_l:.3f}; "
           f"(q rounded twice): o {r2_o:.3f} lse {r2_l:.3f}; max |lse err| {e_l2:.2e} vs {e_2r:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,heads", [("tiny_231", 4), ("connector_1024", 32), ("full_6144", 8)])
+def test_attn_log2q_equals_kernel_scaled(name, heads):
+    w = wl.WORKLOADS[name]
+    print(f"attn_log2q {name} H={heads}", flush=True)
+    q, k, v = (t.to(DEV) for t in wl.qkv(w, heads=heads))
+    B, Nq, H, _ = q.shape
+    c = ltxa.log2_domain_scale(w.scale)
+    q2 = (q.float() * c).to(torch.bfloat16)
+    lse_a = torch.empty((B, H, Nq), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty_like(lse_a)
+    a = ltxa.attn_fwd(q, k, v, nk_valid=w.nk_valid, scale=w.scale, lse=lse_a)
+    b = ltxa.attn_fwd(q2, k, v, nk_valid=w.nk_valid, lse=lse_b, q_log2=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(lse_a.view(-1).cpu().numpy().view(np.uint32),
+                          lse_b.view(-1).cpu().numpy().view(np.uint32))
+
+
+def test_rope_ex_out_scale():
+    # The connector's rotation (grid over the inner dimension of all heads)
+    # with an output scale: 1 is bit-identical to no scale; c sits within the
+    # rotary bar of c times the oracle's rotation.
+    w = wl.WORKLOADS["connector_1024"]
+    print("rope_ex out_scale connector_1024", flush=True)
+    q, _, _ = wl.qkv(w, heads=w.full_heads)
+    pos, _ = wl.positions(w)
+    pg = torch.from_numpy(pos).to(DEV)
+    B, N, H, D = q.shape
+    opts = ltxa.rope_opts(grid_heads=H)
+    plain, one, scaled = (q.to(DEV) for _ in range(3))
+    ltxa.rope(plain, pg, w.q_max_pos, w.theta, opts=opts)
+    ltxa.rope(one, pg, w.q_max_pos, w.theta, opts=opts, out_scale=1.0)
+    c = ltxa.log2_domain_scale(w.scale)
+    ltxa.rope(scaled, pg, w.q_max_pos, w.theta, opts=opts, out_scale=c)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(one), bits(plain))
+    x64 = f64(q)
+    ref = c * oracle.rope_apply(x64, pos, w.q_max_pos, w.theta, grid_heads=H)
+    ok, exact = rope_ok(f64(scaled), ref, c * x64)
+    assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
+    assert exact > 0.995

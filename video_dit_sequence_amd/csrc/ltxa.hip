@@ -54,16 +54,15 @@ ltxa::RopeMode rope_mode(const ltxa_rope_opts* opts) {
     m.inner = opts->grid_heads > 0;
     m.f64 = opts->fp64_angles != 0;
     m.mid = opts->middle ? 0.5 : 0.0;
+    if (opts->out_scale != 0.0f) m.out_scale = opts->out_scale;
   }
   return m;
 }
 
 int rope_launch(const void* src, void* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
                 const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                double theta, const ltxa_rope_opts* opts, void* stream, void* second = nullptr,
-                float out_scale = 1.0f) {
-  ltxa::RopeMode mode = rope_mode(opts);
-  mode.out_scale = out_scale;
+                double theta, const ltxa_rope_opts* opts, void* stream, void* second = nullptr) {
+  const ltxa::RopeMode mode = rope_mode(opts);
   return launch_status(ltxa::launch_rope_any(
       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(second),
       static_cast<uint16_t*>(second), pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
@@ -179,17 +178,13 @@ LTXA_EXPORT int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* 
                      stream);
 }
 
-LTXA_EXPORT int ltxa_sp_pack_rope_scaled(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,
-                                         int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
-                                         int32_t head_dim, int32_t world_size, double theta, float out_scale,
-                                         void* stream) {
-  int rc = ltxa::check_pack_rope(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim, world_size,
-                                 theta);
+LTXA_EXPORT int ltxa_attn_fwd_log2q(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk_pad,
+                                    int64_t nk_valid, void* stream) {
+  const int rc = ltxa::check_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid, 1.0f);
   if (rc) return rc;
-  rc = ltxa::check_out_scale(out_scale);
-  if (rc) return rc;
-  return rope_launch(src, dst, pos, n_tokens, axes, max_pos, batch, heads, head_dim, world_size, theta, nullptr,
-                     stream, nullptr, out_scale);
+  return launch_status(ltxa::launch_attn(q, k, v, o, lse, batch, heads, head_dim, nq, nk_pad, nk_valid, 1.0f,
+                                         batch, heads, static_cast<hipStream_t>(stream), true));
 }
 
 LTXA_EXPORT int ltxa_attn_fwd_unpack_log2q(const void* q, const void* k, const void* v, void* o, float* lse,

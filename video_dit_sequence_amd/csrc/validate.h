@@ -154,11 +154,6 @@ inline int check_pack_rope(const void* src, const void* dst, const int32_t* pos,
   return LTXA_OK;
 }
 
-// Output scale of the scaled rotary pack: finite and positive.
-inline int check_out_scale(float out_scale) {
-  return std::isfinite(out_scale) && out_scale > 0.0f ? LTXA_OK : LTXA_E_SHAPE;
-}
-
 // Attention over world_size head shards [world_size, batch, n, heads/world_size,
 // head_dim] with the output in the token-major [batch, nq, heads, head_dim]
 // layout: the same checks as check_attn over a batch of world_size * batch
@@ -175,13 +170,19 @@ inline int check_attn_unpack(const void* q, const void* k, const void* v, const 
                     nk_valid, scale);
 }
 
+// Output scale of the rotary calls (ltxa_rope_opts::out_scale when not 0):
+// finite and positive.
+inline int check_out_scale(float out_scale) {
+  return std::isfinite(out_scale) && out_scale > 0.0f ? LTXA_OK : LTXA_E_SHAPE;
+}
+
 // Options of the rotary variants; opts may be NULL (all zero).
 inline int check_rope_opts(const ltxa_rope_opts* opts, int32_t heads, int32_t head_dim, int32_t axes) {
   if (!opts) return LTXA_OK;
   if (!(opts->rope_type == LTXA_ROPE_INTERLEAVED || opts->rope_type == LTXA_ROPE_SPLIT)) return LTXA_E_SHAPE;
   if (!(opts->fp64_angles == 0 || opts->fp64_angles == 1)) return LTXA_E_SHAPE;
   if (!(opts->middle == 0 || opts->middle == 1)) return LTXA_E_SHAPE;
-  if (opts->reserved != 0) return LTXA_E_SHAPE;
+  if (opts->out_scale != 0.0f && check_out_scale(opts->out_scale) != LTXA_OK) return LTXA_E_SHAPE;
   if (opts->grid_heads < 0 || opts->head_offset < 0) return LTXA_E_SHAPE;
   if (opts->grid_heads > 0) {
     if (int64_t(opts->head_offset) + heads > opts->grid_heads) return LTXA_E_SHAPE;

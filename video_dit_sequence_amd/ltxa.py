@@ -36,7 +36,7 @@ LTXA_E_RANGE = -7
 
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
            "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
-           "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_sp_pack_rope_scaled",
+           "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_attn_fwd_log2q",
            "ltxa_attn_fwd_unpack_log2q")
 
 LTXA_ROPE_INTERLEAVED = 0
@@ -47,20 +47,21 @@ class RopeOpts(ctypes.Structure):
     """``ltxa_rope_opts``: the rotary variants (see ``include/ltxa.h``)."""
     _fields_ = [("rope_type", ctypes.c_int32), ("grid_heads", ctypes.c_int32),
                 ("head_offset", ctypes.c_int32), ("fp64_angles", ctypes.c_int32),
-                ("middle", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("middle", ctypes.c_int32), ("out_scale", ctypes.c_float)]
 
 
 def rope_opts(rope_type: str = "interleaved", grid_heads: int = 0, head_offset: int = 0,
-              fp64_angles: bool = False, middle: bool = False) -> RopeOpts:
+              fp64_angles: bool = False, middle: bool = False, out_scale: float = 0.0) -> RopeOpts:
     """Build an ``ltxa_rope_opts``.  ``rope_type`` is "interleaved" or "split";
     ``grid_heads = 0`` shares one head_dim-wide grid across heads, ``G > 0``
     lays the grid over ``G`` heads (head ``j`` of a tensor is grid head
-    ``head_offset + j``)."""
+    ``head_offset + j``).  ``out_scale`` (0: none) multiplies every output
+    value before its one rounding to bf16."""
     types = {"interleaved": LTXA_ROPE_INTERLEAVED, "split": LTXA_ROPE_SPLIT}
     if rope_type not in types:
         raise ValueError("rope_type must be 'interleaved' or 'split'")
     return RopeOpts(types[rope_type], int(grid_heads), int(head_offset), int(bool(fp64_angles)),
-                    int(bool(middle)), 0)
+                    int(bool(middle)), float(out_scale))
 
 
 class LtxaError(RuntimeError):
@@ -109,9 +110,8 @@ def lib() -> ctypes.CDLL:
         L.ltxa_attn_fwd_unpack.restype = ctypes.c_int
         L.ltxa_attn_fwd_unpack.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                            ctypes.c_float, i32, vp]
-        L.ltxa_sp_pack_rope_scaled.restype = ctypes.c_int
-        L.ltxa_sp_pack_rope_scaled.argtypes = [vp, vp, vp, i64, i32, dp, i64, i32, i32, i32,
-                                               ctypes.c_double, ctypes.c_float, vp]
+        L.ltxa_attn_fwd_log2q.restype = ctypes.c_int
+        L.ltxa_attn_fwd_log2q.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64, vp]
         L.ltxa_attn_fwd_unpack_log2q.restype = ctypes.c_int
         L.ltxa_attn_fwd_unpack_log2q.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                                  i32, vp]
@@ -211,11 +211,14 @@ def rope_qk(q: Optional[torch.Tensor], q_pos: Optional[torch.Tensor], q_max_pos,
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Optional[int] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+             lse: Optional[torch.Tensor] = None, q_log2: bool = False) -> torch.Tensor:
     """Masked attention (``ltxa_attn_fwd``) over bf16 BSHD tensors.
 
     Keys ``>= nk_valid`` (default: all) are excluded.  ``scale`` defaults to
     ``1/sqrt(D)``.  ``lse``, if given, is a float32 ``[B, H, Nq]`` tensor.
+    With ``q_log2`` the queries are already multiplied by ``scale * log2(e)``
+    (:func:`log2_domain_scale`) and ``scale`` is not used
+    (``ltxa_attn_fwd_log2q``).
     """
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _gpu(t, name, torch.bfloat16)
@@ -236,17 +239,23 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Option
         if lse.shape != (B, H, Nq):
             raise ValueError("lse must be [B, H, Nq]")
         lse_ptr = lse.data_ptr()
-    _check("ltxa_attn_fwd", lib().ltxa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                                out.data_ptr(), lse_ptr, B, H, D, Nq, Nk, nk_valid,
-                                                scale, _stream_ptr(q)))
+    if q_log2:
+        _check("ltxa_attn_fwd_log2q", lib().ltxa_attn_fwd_log2q(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, H, D, Nq, Nk, nk_valid,
+            _stream_ptr(q)))
+    else:
+        _check("ltxa_attn_fwd", lib().ltxa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                    out.data_ptr(), lse_ptr, B, H, D, Nq, Nk, nk_valid,
+                                                    scale, _stream_ptr(q)))
     return out
 
 
 def rope(x: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
-         opts: Optional[RopeOpts] = None) -> None:
+         opts: Optional[RopeOpts] = None, out_scale: Optional[float] = None) -> None:
     """Rotate bf16 ``x`` (``[B, N, H, D]``) in place with the variants of
     ``opts`` (:func:`rope_opts`; ``None`` = the rotation of :func:`rope_qk`)
-    (``ltxa_rope_ex``)."""
+    (``ltxa_rope_ex``).  ``out_scale`` overrides ``opts.out_scale``."""
+    opts = _with_scale(opts, out_scale)
     _gpu(x, "x", torch.bfloat16)
     _gpu(pos, "pos", torch.int32)
     if x.dim() != 4:
@@ -257,6 +266,15 @@ def rope(x: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
     _check("ltxa_rope_ex", lib().ltxa_rope_ex(
         x.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos), B, H, D, float(theta),
         None if opts is None else ctypes.byref(opts), _stream_ptr(x)))
+
+
+def _with_scale(opts: Optional[RopeOpts], out_scale: Optional[float]) -> Optional[RopeOpts]:
+    """``opts`` with ``out_scale`` set (a copy; ``opts`` None: the defaults)."""
+    if out_scale is None:
+        return opts
+    o = rope_opts() if opts is None else RopeOpts.from_buffer_copy(opts)
+    o.out_scale = float(out_scale)
+    return o
 
 
 def log2_domain_scale(scale: float) -> float:
@@ -271,8 +289,7 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
                  theta: float = 10000.0, out: Optional[torch.Tensor] = None,
                  opts: Optional[RopeOpts] = None, out_scale: Optional[float] = None) -> torch.Tensor:
     """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` (``ltxa_sp_pack_rope``,
-    ``ltxa_sp_pack_rope_ex`` when ``opts`` is given, ``ltxa_sp_pack_rope_scaled``
-    when ``out_scale`` is).
+    or ``ltxa_sp_pack_rope_ex`` when ``opts`` or ``out_scale`` is given).
 
     Equal, bit for bit, to :func:`sp_pack` followed by the rotation of each
     rank's shard.  ``pos`` is an int32 ``[N, A]`` GPU tensor.  ``out_scale``
@@ -291,13 +308,8 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
     _gpu(out, "out", torch.bfloat16)
     if out.numel() != src.numel():
         raise ValueError("out has the wrong number of elements")
-    if out_scale is not None:
-        if opts is not None:
-            raise ValueError("out_scale applies to the default rotation only (opts must be None)")
-        _check("ltxa_sp_pack_rope_scaled", lib().ltxa_sp_pack_rope_scaled(
-            src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
-            B, H, D, P, float(theta), float(out_scale), _stream_ptr(src)))
-    elif opts is None:
+    opts = _with_scale(opts, out_scale)
+    if opts is None:
         _check("ltxa_sp_pack_rope", lib().ltxa_sp_pack_rope(
             src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
             B, H, D, P, float(theta), _stream_ptr(src)))
@@ -458,7 +470,7 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     exchanged, and attention writes token order directly
     (``ltxa_attn_fwd_unpack``).  With ``prescale_q`` (the default) the Q pass
     also multiplies by ``scale * log2(e)`` before its one rounding
-    (``ltxa_sp_pack_rope_scaled``) and the attention takes those queries as
+    (``ltxa_sp_pack_rope_ex`` with ``out_scale``) and the attention takes those queries as
     given (``ltxa_attn_fwd_unpack_log2q``): Q is rounded once instead of
     twice.  With ``prescale_q=False`` the fused result is bit-identical to the
     unfused one.
@@ -499,7 +511,7 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
 def connector_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, max_pos,
                         nk_valid: Optional[int] = None, theta: float = 10000.0,
                         rope_type: str = "interleaved", fp64_angles: bool = False,
-                        scale: Optional[float] = None) -> torch.Tensor:
+                        scale: Optional[float] = None, prescale_q: bool = True) -> torch.Tensor:
     """The attention core of the 1D text connector (FastVideo gemma page,
     ``Embeddings1DConnector.forward``): rotate Q and K in place by 1D
     positions with the grid over the inner dimension (all ``H`` heads,
@@ -509,9 +521,17 @@ def connector_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: 
     parallelism); ``pos``: int32 ``[N, 1]``; an additive mask with a valid
     prefix of ``nk_valid`` keys is ``nk_valid`` (default: all keys, as after
     the learnable registers replace the padding).  Returns ``[B, N, H, D]``.
+    With ``prescale_q`` (the default) Q's rotation also multiplies by
+    ``scale * log2(e)`` before its one rounding and the attention takes Q as
+    given (``ltxa_attn_fwd_log2q``), so Q is rounded once; Q then holds those
+    log2-domain values.
     """
-    H = q.shape[2]
+    H, D = q.shape[2], q.shape[3]
     opts = rope_opts(rope_type=rope_type, grid_heads=H, fp64_angles=fp64_angles)
-    rope(q, pos, max_pos, theta, opts=opts)
+    if prescale_q:
+        c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale))
+        rope(q, pos, max_pos, theta, opts=opts, out_scale=c)
+    else:
+        rope(q, pos, max_pos, theta, opts=opts)
     rope(k, pos, max_pos, theta, opts=opts)
-    return attn_fwd(q, k, v, nk_valid=nk_valid, scale=scale)
+    return attn_fwd(q, k, v, nk_valid=nk_valid, scale=scale, q_log2=prescale_q)
