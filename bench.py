@@ -352,7 +352,9 @@ def main():
         "data": "synthetic" if args.inputs == "normal" else "synthetic, all zeros (diagnostic, not a result)",
         "config": {"workload": WORKLOAD, "tokens": N, "valid_tokens": w.nq_valid, "heads": H,
                    "head_dim": D, "virtual_ranks": P, "heads_per_rank": Hl, "batch": B,
-                   "grid_txy": list(w.q_grid), "rope_theta": w.theta, "path": args.path},
+                   "grid_txy": list(w.q_grid), "rope_theta": w.theta, "path": args.path,
+                   "q_operand": ("log2-domain (the rotary pack multiplies by scale*log2(e) before its one rounding)"
+                                 if args.path == "fused" else "scaled and rounded inside the attention kernel")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "attn_fwd_kernel<128, 8>",
