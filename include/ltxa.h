@@ -254,10 +254,10 @@ typedef struct ltxa_rope_opts {
  *   rotated one rank at a time (head_offset = rank * heads per rank), or
  *   through ltxa_sp_pack_rope_ex.
  * Errors: as ltxa_rope_qk for one tensor, plus E_NULL (pos or max_pos NULL),
- * E_SHAPE (rope_type, fp64_angles or middle not 0/1, out_scale neither 0
- * nor finite and > 0,
- * grid_heads < 0, head_offset < 0 or head_offset + heads > grid_heads, or
- * fewer grid pairs than axes), E_ALIGN (SPLIT with head_dim % 16 != 0).
+ * E_SHAPE (rope_type, fp64_angles or middle not 0/1; out_scale neither 0
+ * nor finite and > 0; grid_heads < 0, head_offset < 0 or head_offset +
+ * heads > grid_heads; fewer grid pairs than axes), E_ALIGN (SPLIT with
+ * head_dim % 16 != 0).
  */
 int ltxa_rope_ex(void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
                  const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim,
