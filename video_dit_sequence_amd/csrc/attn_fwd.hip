@@ -7,10 +7,13 @@
 // Work split.  One workgroup = W waves = 32 W query rows of one (batch,
 // head); each wave owns 32 query rows for the whole key loop.  At least two
 // waves share each SIMD, so one wave's softmax (VALU) runs while another's
-// matrix instructions execute.  D = 128 uses 8-wave workgroups (255
+// matrix instructions execute.  D = 128 uses 8-wave workgroups (256
 // registers per lane: one workgroup per CU, two waves per SIMD); D = 64 uses
 // 4-wave workgroups held to 168 registers, three per CU, which overlap each
-// other's start and end (the D = 64 workloads have short key loops).  Keys
+// other's start and end (the D = 64 workloads have short key loops).
+// attn_fwd_kernel below is the D = 64 kernel, on 32x32x16 products;
+// attn_fwd16_kernel, further down, is the D = 128 one, on 16x16x32 products
+// (same structure; its own comment gives the lane layout).  Keys
 // stream through LDS in tiles of 64 keys, double-buffered: while tile i is
 // consumed, tile i+1 is copied global -> LDS directly (buffer_load ... lds,
 // no register staging).
@@ -497,6 +500,348 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Value of x held by lane l ^ mask, through the LDS crossbar.
+__device__ __forceinline__ float xlane(float x, int mask) {
+  const int addr = ((__lane_id() ^ mask) << 2);
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
+
+// Head dimension 128: the same tiling, ring, softmax and output staging as
+// attn_fwd_kernel, with the products on v_mfma_f32_16x16x32_bf16.  Measured on
+// MI355X, that instruction sustains 15 % more TFLOP/s than the 32x32x16 one
+// on random operands (the clock falls less under its power draw: a 32-head
+// 32768-token launch ran at 2.0 GHz instead of 1.7), at the cost of twice the
+// matrix instructions (~16 % more cycles in this kernel); the net gain on
+// that launch is 0.5-2.4 % box to box, 2-4 % on shorter key loops.
+//
+// Lane l = 16 g + j (g = l / 16) supplies row j of A and column j of B, each
+// as 8 k values of k-slice g, and receives column j of C, rows 4 g + r in
+// accumulator register r.  Per wave: 32 queries as two 16-query blocks qb;
+// per 64-key tile, four 16-key blocks kb.  The S^T block (kb, qb) =
+// K[16 kb .. 16 kb + 15] * Q^T[qb] leaves lane l with query 16 qb + j and keys
+// 16 kb + 4 g + r.  P^T for the 32-key chunk kc and block qb is those of key
+// blocks 2 kc and 2 kc + 1, as k values 0..3 and 4..7 of slice g: keys
+// {32 kc + 4 g + r, 32 kc + 16 + 4 g + r}, straight from the accumulators; V^T
+// is read in the same key order with two transpose reads per fragment.  A
+// query's 64 keys of a tile sit in the four lanes j, 16 + j, 32 + j, 48 + j,
+// so its row statistics take two exchanges (only for the first tile, a
+// rescale and the final sum).
+template <int W>
+__global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
+    int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
+    int32_t out_heads) {
+  constexpr int D = 128;
+  constexpr int kThreads = W * 64;
+  constexpr int kBQ = W * kQW;          // query rows per workgroup
+  constexpr int KS = D / 32;            // 32-channel steps of K Q^T
+  constexpr int CB = D / 16;            // 16-channel blocks of O^T
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROW = D * 2;            // bytes per K/V row
+  constexpr int TILE = kBK * ROW;       // bytes per K or V tile
+  constexpr int LOADS = TILE / (kThreads * 16);
+  static_assert(LOADS * kThreads * 16 == TILE, "tile copy covers the tile");
+
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE], sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE], sV1[TILE];
+
+  const int lid = xcd_contiguous(blockIdx.x, nblocks);
+  const int bh = lid / qblocks;
+  const int qb0 = lid - bh * qblocks;
+  const int64_t b = bh / heads;
+  const int64_t h = bh - b * heads;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int64_t rs = int64_t(heads) * D;
+  const __bf16* qbase = q + (b * nq * heads + h) * D;
+  const __bf16* kbase = k + (b * nk_pad * heads + h) * D;
+  const __bf16* vbase = v + (b * nk_pad * heads + h) * D;
+  const int32_t ob = static_cast<int32_t>(b) % out_batch, op = static_cast<int32_t>(b) / out_batch;
+  __bf16* obase = o + ((int64_t(ob) * nq * out_heads) + int64_t(op) * heads + h) * D;
+  float* lbase = lse ? lse + (b * heads + h) * nq : nullptr;
+  asm volatile("" : "+s"(obase), "+s"(lbase));
+  const int64_t ors = int64_t(out_heads) * D;
+
+  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
+  const int full_tiles = static_cast<int>(nk_valid / kBK);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t cp_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int s = (wave * LOADS + i) * 64 + lane;
+    const int row = s / CH;
+    cp_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
+  }
+  auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
+    const int64_t first = int64_t(t) * kBK;
+    const int64_t rows = nk_valid - first < kBK ? nk_valid - first : kBK;
+    const uint32_t extent = static_cast<uint32_t>((rows - 1) * rs * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbase + first * rs, extent);
+    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbase + first * rs, extent);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + i) * 1024);
+      LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + i) * 1024);
+      dma16(rk, kd, cp_off[i]);
+      dma16(rv, vd, cp_off[i]);
+    }
+  };
+  {
+    char* const ring[4] = {sK0, sK1, sV0, sV1};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        *reinterpret_cast<u32x4*>(ring[r] + (wave * LOADS + i) * 1024 + lane * 16) = u32x4{};
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+  issue_tile(0, sK0, sV0);
+
+  // Q^T operands: block qb holds query row q0 + 32 wave + 16 qb + j, channels 32 s + 8 g .. +7.
+  const int64_t qrow0 = int64_t(qb0) * kBQ + wave * kQW + j;
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t qrow = qrow0 + 16 * qb;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 x = qrow < nq ? *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 32 + g * 8) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * scale_log2);
+      qf[qb][s] = x;
+    }
+  }
+
+  // LDS offsets.  K fragment (A of S^T) for key block kb, step s: row 16 kb + j, chunk 4 s + g
+  // at position (4 s + g) ^ swz(row); swz depends on row % 16 = j.  V fragment (A of O^T) for
+  // channel block cb, key chunk kc: transpose reads of rows 32 kc + 4 g + j / 4 (and + 16),
+  // columns 16 cb + 4 (j % 4); row % 16 = 4 g + j / 4 for all of them.
+  int k_off[KS], v_off[CB];
+  {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k_off[s] = j * ROW + (((4 * s + g) ^ swz<D>(j)) << 4);
+    const int vr = 4 * g + (j >> 2);
+    const int vs = swz<D>(vr);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      v_off[cb] = vr * ROW + (j & 1) * 8 + (((2 * cb + ((j & 3) >> 1)) ^ vs) << 4);
+  }
+
+  f32x4 acc[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{};
+  float m[2] = {0.0f, 0.0f};
+  float l[2] = {0.0f, 0.0f};
+  f32x4 neg_m[2] = {f32x4{}, f32x4{}};
+
+  auto compute_tile = [&] __device__(int t, const char* cK, const char* cV, auto masked, auto first)
+                          __attribute__((always_inline)) {
+    const LDS_AS char* lK = (const LDS_AS char*)cK;
+    const LDS_AS char* lV = (const LDS_AS char*)cV;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(k_off[s]));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(v_off[cb]));
+    f32x4 sc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb][0] = neg_m[0], sc[kb][1] = neg_m[1];
+    __builtin_amdgcn_s_setprio(1);
+    {
+      bf16x8 kf[4 * KS];
+#pragma unroll
+      for (int i = 0; i < 4 * KS; ++i)
+        kf[i] = *(const LDS_AS bf16x8*)(lK + (i & 3) * 16 * ROW + k_off[i >> 2]);
+#pragma unroll
+      for (int i = 0; i < 4 * KS; ++i) {
+        sc[i & 3][0] = mfma16(kf[i], qf[0][i >> 2], sc[i & 3][0]);
+        sc[i & 3][1] = mfma16(kf[i], qf[1][i >> 2], sc[i & 3][1]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * KS - kKAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kKAhead, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (decltype(masked)::value != 0) {
+      // Key of register r in block kb is 16 kb + 4 g + r.
+      const int lim = static_cast<int>(nk_valid - int64_t(t) * kBK) - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kb + r >= lim) sc[kb][0][r] = sc[kb][1][r] = -INFINITY;
+    }
+    auto tile_max = [&] __device__(int qb) __attribute__((always_inline)) {
+      float a = fmaxf(sc[0][qb][0], sc[1][qb][0]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a = fmaxf(a, sc[kb][qb][r]);
+      a = fmaxf(a, xlane(a, 16));
+      return fmaxf(a, xlane(a, 32));  // tile max of the query, relative to m
+    };
+    auto shift = [&] __device__(float d0, float d1) __attribute__((always_inline)) {
+      m[0] += d0;
+      m[1] += d1;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc[kb][0][r] -= d0;
+          sc[kb][1][r] -= d1;
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        neg_m[0][r] = -m[0];
+        neg_m[1][r] = -m[1];
+      }
+    };
+    if constexpr (decltype(first)::value != 0) shift(tile_max(0), tile_max(1));
+    float sum0 = 0.0f, sum1 = 0.0f;
+    bf16x8 pf[2][2];
+    auto probs = [&] __device__() __attribute__((always_inline)) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a0 = __builtin_amdgcn_exp2f(sc[2 * kc][0][r]);
+          const float a1 = __builtin_amdgcn_exp2f(sc[2 * kc + 1][0][r]);
+          const float b0 = __builtin_amdgcn_exp2f(sc[2 * kc][1][r]);
+          const float b1 = __builtin_amdgcn_exp2f(sc[2 * kc + 1][1][r]);
+          pf[kc][0][r] = static_cast<__bf16>(a0);
+          pf[kc][0][r + 4] = static_cast<__bf16>(a1);
+          pf[kc][1][r] = static_cast<__bf16>(b0);
+          pf[kc][1][r + 4] = static_cast<__bf16>(b1);
+          s0 += a0;
+          s0 += a1;
+          s1 += b0;
+          s1 += b1;
+        }
+      sum0 = s0;
+      sum1 = s1;
+    };
+    probs();
+    const uint32_t worst = (__builtin_bit_cast(uint32_t, sum0) & 0x7fffffffu) >
+                                   (__builtin_bit_cast(uint32_t, sum1) & 0x7fffffffu)
+                               ? (__builtin_bit_cast(uint32_t, sum0) & 0x7fffffffu)
+                               : (__builtin_bit_cast(uint32_t, sum1) & 0x7fffffffu);
+    if (__builtin_amdgcn_ballot_w64(worst >= kSumGuardBits)) {
+      const float d0 = fmaxf(tile_max(0), 0.0f), d1 = fmaxf(tile_max(1), 0.0f);
+      const float a0 = __builtin_amdgcn_exp2f(-d0), a1 = __builtin_amdgcn_exp2f(-d1);
+      l[0] *= a0;
+      l[1] *= a1;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        acc[cb][0] *= a0;
+        acc[cb][1] *= a1;
+      }
+      shift(d0, d1);
+      probs();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 vf[2 * CB];
+#pragma unroll
+    for (int i = 0; i < 2 * CB; ++i) {
+      const int kc = i / CB, cb = i % CB;
+      vf[i] = lds_tr_pair(lV + kc * 32 * ROW + v_off[cb], lV + kc * 32 * ROW + 16 * ROW + v_off[cb]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * CB; ++i) {
+      const int kc = i / CB, cb = i % CB;
+      acc[cb][0] = mfma16(vf[i], pf[kc][0], acc[cb][0]);
+      acc[cb][1] = mfma16(vf[i], pf[kc][1], acc[cb][1]);
+    }
+    l[0] += sum0;
+    l[1] += sum1;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVAhead, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * CB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+      if (i + kVAhead < 2 * CB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  char* const ringK[kStages] = {sK0, sK1};
+  char* const ringV[kStages] = {sV0, sV1};
+  auto iteration = [&] __device__(int t, auto st, auto masked, auto first) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int S1 = (ST + 1) % kStages;
+    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
+    compute_tile(t, ringK[ST], ringV[ST], masked, first);
+  };
+  if (full_tiles >= 1)
+    iteration(0, Int<0>{}, Int<0>{}, Int<1>{});
+  else
+    iteration(0, Int<0>{}, Int<1>{}, Int<1>{});
+  int t = 1;
+  for (; t + 2 <= full_tiles; t += 2) {
+    iteration(t, Int<1>{}, Int<0>{}, Int<0>{});
+    iteration(t + 1, Int<0>{}, Int<0>{}, Int<0>{});
+  }
+  if (t < full_tiles) {
+    iteration(t, Int<1>{}, Int<0>{}, Int<0>{});
+    if (t + 1 < ntiles) iteration(t + 1, Int<0>{}, Int<1>{}, Int<0>{});
+  } else if (t < ntiles) {
+    iteration(t, Int<1>{}, Int<1>{}, Int<0>{});
+  }
+
+  float lt[2], inv[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float x = l[qb] + xlane(l[qb], 16);
+    lt[qb] = x + xlane(x, 32);
+    inv[qb] = 1.0f / lt[qb];
+  }
+  if (lbase && g == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      if (qrow0 + 16 * qb < nq) lbase[qrow0 + 16 * qb] = (m[qb] + __builtin_log2f(lt[qb])) * 0.69314718055994531f;
+  }
+
+  static_assert(2 * kQW == kBK && W <= 8, "two waves' output tiles fill one ring stage");
+  __syncthreads();
+  char* const stage = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sV0 : sV1) + (wave & 1) * (kQW * ROW);
+  // Lane l holds, for local row 16 qb + j, channels 16 cb + 4 g .. + 3: 8 bytes of chunk
+  // 2 cb + g / 2, half g % 2.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = 16 * qb + j;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const u32x2 w = {pack_bf16x2(acc[cb][qb][0] * inv[qb], acc[cb][qb][1] * inv[qb]),
+                       pack_bf16x2(acc[cb][qb][2] * inv[qb], acc[cb][qb][3] * inv[qb])};
+      const int c = 2 * cb + (g >> 1);
+      *reinterpret_cast<u32x2*>(stage + r * ROW + ((c ^ (r % CH)) << 4) + (g & 1) * 8) = w;
+    }
+  }
+  __syncthreads();
+  constexpr int RPI = 64 / CH;
+  const int64_t q0 = int64_t(qb0) * kBQ + wave * kQW;
+#pragma unroll
+  for (int i = 0; i < kQW / RPI; ++i) {
+    const int r = i * RPI + lane / CH, c = lane % CH;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * ROW + ((c ^ (r % CH)) << 4));
+    if (q0 + r < nq) *reinterpret_cast<u32x4*>(obase + (q0 + r) * ors + c * 8) = w;
+  }
+}
+
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch,
                     int32_t heads, int64_t nq, int64_t nk_pad, int64_t nk_valid, float scale,
@@ -512,7 +857,13 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Log2-domain q is taken as given: x * 1.0f rounded to bf16 is x.
   const float scale_log2 = q_log2 ? 1.0f : static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, W>), dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
+  auto kernel = [] {
+    if constexpr (D == 128)
+      return attn_fwd16_kernel<W>;
+    else
+      return attn_fwd_kernel<D, W>;
+  }();
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nq, nk_pad, nk_valid,
                      heads, static_cast<int32_t>(qblocks), static_cast<int32_t>(nblocks), scale_log2,
