@@ -38,9 +38,9 @@
 // group receives element j of each of the 4 rows.
 //
 // LDS layout.  K and V tiles are row-major [64 keys][D] with the 16-byte
-// chunks of row r permuted by XOR with swz(r), so that the 32 rows read by
-// one K fragment and the 4 rows read by one V transpose read fall in
-// different banks.
+// chunks of row r permuted by XOR with a function of r (swz64 here; swz_k16
+// and swz_v16 for the head-dimension-128 kernel), so that the rows read by
+// one K fragment or one V transpose read fall in different banks.
 //
 // Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once;
 // or it arrives so multiplied, from the rotary pack, and is used as given),
@@ -114,25 +114,15 @@ __device__ __forceinline__ float partner(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
 
-// Chunk permutation of LDS row r (16-byte chunks).  D = 128: 16 chunks per
-// 256-byte row; the 16 rows r..r+15 of a K fragment read put one chunk in 16
-// distinct positions, and the 4 consecutive rows of a V transpose read
-// (which take 2 adjacent chunks each) land 4 positions apart.  Measured on
-// MI355X with SQ_LDS_BANK_CONFLICT: zero conflict cycles for both reads.
-// D = 64: 8 chunks per 128-byte row, two rows per 256-byte bank window, so a
-// chunk's bank group is 8 (r & 1) + its position.  The permutation takes
-// each half (even rows, odd rows) of r..r+15 to 8 distinct positions (K
-// fragment reads), and gives rows r and r + 2 of a V transpose read
-// permutations that differ in bit 2, so that their chunks 0..3 (or 4..7)
-// fall in disjoint bank groups.  The earlier choice let those rows collide:
-// 1.34e7 conflict cycles per cross-attention launch, now 7.9e5.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128)
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  else
-    return ((r >> 2) & 3) | (((r >> 1) & 1) << 2);
-}
+// Chunk permutation of LDS row r (16-byte chunks) for head dimension 64:
+// 8 chunks per 128-byte row, two rows per 256-byte bank window, so a chunk's
+// bank group is 8 (r & 1) + its position.  The permutation takes each half
+// (even rows, odd rows) of r..r+15 to 8 distinct positions (K fragment
+// reads), and gives rows r and r + 2 of a V transpose read permutations that
+// differ in bit 2, so that their chunks 0..3 (or 4..7) fall in disjoint bank
+// groups.  The earlier choice let those rows collide: 1.34e7 conflict cycles
+// per cross-attention launch, now 7.9e5.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 2) & 3) | (((r >> 1) & 1) << 2); }
 
 // One 16-byte-per-lane copy global -> LDS through buffer resource r: lane l
 // reads byte offset voff and writes LDS bytes [dst + 16 l, +16).  (Kept out
@@ -170,6 +160,7 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
     int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
     int32_t out_heads) {
+  static_assert(D == 64, "head dimension 128 runs on attn_fwd16_kernel");
   constexpr int kThreads = W * 64;
   constexpr int kBQ = W * kQW;          // query rows per workgroup
   constexpr int KS = D / 16;            // 16-channel steps of K Q^T
@@ -224,7 +215,7 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   for (int j = 0; j < LOADS; ++j) {
     const int s = (wave * LOADS + j) * 64 + lane;
     const int row = s / CH;
-    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
+    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz64(row)) * 8) * 2);
   }
   auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
     const int64_t first = int64_t(t) * kBK;
@@ -280,14 +271,14 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   // 32d + 16(g%2) + 4(gi%4).
   int k_off[KS], v_off0[DB], v_off1[DB];
   {
-    const int k_x = hf ^ swz<D>(ln);
+    const int k_x = hf ^ swz64(ln);
 #pragma unroll
     for (int s = 0; s < KS; ++s) k_off[s] = ln * ROW + (((2 * s) ^ k_x) << 4);
     const int g = lane >> 4, gi = lane & 15;
     const int v_row0 = 4 * (g >> 1) + (gi >> 2);
     const int v_c = 2 * (g & 1) + ((gi & 3) >> 1);
-    const int v_x0 = v_c ^ swz<D>(v_row0);
-    const int v_x1 = v_c ^ swz<D>(v_row0 + 8);
+    const int v_x0 = v_c ^ swz64(v_row0);
+    const int v_x1 = v_c ^ swz64(v_row0 + 8);
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       v_off0[d] = v_row0 * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x0) << 4);
@@ -510,6 +501,24 @@ __device__ __forceinline__ float xlane(float x, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
 
+// Chunk permutations of the K and V tiles for head dimension 128 (16 chunks
+// of 16 bytes per 256-byte row), one per tensor because the two fragment
+// reads of attn_fwd16_kernel need different ones.  Chunk c of row r is
+// stored at position c ^ swz(r).
+// - K: a fragment read gives lane 16 g + j row j (mod 16), chunk 4 s + g.
+//   With position c ^ (r % 16) these 128-bit reads run without bank
+//   conflicts (measured with SQ_LDS_BANK_CONFLICT on MI355X).
+// - V: a transpose read is served one 32-lane half at a time, over the 64
+//   four-byte banks.  A half reads 8 consecutive rows (0..7 or 8..15 mod 16),
+//   8 bytes of each of two adjacent chunks {2a, 2a + 1} per row.  swz_v16
+//   sends that chunk pair of row r to the position pair a ^ (r % 8), so the 8
+//   rows cover all 64 banks once.
+// One permutation shared by both tiles (the 32x32x16 kernel's) cost 4
+// conflict cycles per K read and 2 per V read here: 128 per wave and tile,
+// and 4 % of the 32-head 32768-token launch.
+__device__ __forceinline__ int swz_k16(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
 // Head dimension 128: the same tiling, ring, softmax and output staging as
 // attn_fwd_kernel, with the products on v_mfma_f32_16x16x32_bf16.  Measured on
 // MI355X, that instruction sustains 15 % more TFLOP/s than the 32x32x16 one
@@ -572,12 +581,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
   const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
   const int full_tiles = static_cast<int>(nk_valid / kBK);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t cp_off[LOADS];
+  // Tile copy as in attn_fwd_kernel; K and V tiles take different chunk
+  // permutations (swz_k16, swz_v16), so each lane has a source offset per tensor.
+  uint32_t cpk_off[LOADS], cpv_off[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int s = (wave * LOADS + i) * 64 + lane;
     const int row = s / CH;
-    cp_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz<D>(row)) * 8) * 2);
+    cpk_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_k16(row)) * 8) * 2);
+    cpv_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_v16(row)) * 8) * 2);
   }
   auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
     const int64_t first = int64_t(t) * kBK;
@@ -589,8 +601,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
     for (int i = 0; i < LOADS; ++i) {
       LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + i) * 1024);
       LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + i) * 1024);
-      dma16(rk, kd, cp_off[i]);
-      dma16(rv, vd, cp_off[i]);
+      dma16(rk, kd, cpk_off[i]);
+      dma16(rv, vd, cpv_off[i]);
     }
   };
   {
@@ -620,15 +632,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
   }
 
   // LDS offsets.  K fragment (A of S^T) for key block kb, step s: row 16 kb + j, chunk 4 s + g
-  // at position (4 s + g) ^ swz(row); swz depends on row % 16 = j.  V fragment (A of O^T) for
-  // channel block cb, key chunk kc: transpose reads of rows 32 kc + 4 g + j / 4 (and + 16),
-  // columns 16 cb + 4 (j % 4); row % 16 = 4 g + j / 4 for all of them.
+  // at position (4 s + g) ^ swz_k16(row), which depends on row % 16 = j.  V fragment (A of
+  // O^T) for channel block cb, key chunk kc: transpose reads of rows 32 kc + 4 g + j / 4 (and
+  // + 16), columns 16 cb + 4 (j % 4); row % 16 = 4 g + j / 4 for all of them.
   int k_off[KS], v_off[CB];
   {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) k_off[s] = j * ROW + (((4 * s + g) ^ swz<D>(j)) << 4);
+    for (int s = 0; s < KS; ++s) k_off[s] = j * ROW + (((4 * s + g) ^ swz_k16(j)) << 4);
     const int vr = 4 * g + (j >> 2);
-    const int vs = swz<D>(vr);
+    const int vs = swz_v16(vr);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       v_off[cb] = vr * ROW + (j & 1) * 8 + (((2 * cb + ((j & 3) >> 1)) ^ vs) << 4);
