@@ -17,8 +17,8 @@ rounds Q itself.
 
 Prints one JSON line.  ``value`` is attention TFLOP/s over the whole step
 (4 * Nq * Nk_valid * D * H flop per step).  ``roofline`` covers the dominant
-kernel (attn_fwd16_kernel, launched by ltxa_attn_fwd_unpack_log2q), timed with HIP events on its own stream inside the
-timed region.  ``cpu_baseline`` is the fp64 numpy oracle on a bounded row
+kernel (attn_fwd_kernel<128, 8>, launched by ltxa_attn_fwd_unpack_log2q), timed
+with HIP events on its own stream inside the timed region.  ``cpu_baseline`` is the fp64 numpy oracle on a bounded row
 sample of the same workload.
 """
 
@@ -357,7 +357,7 @@ def main():
                                  if args.path == "fused" else "scaled and rounded inside the attention kernel")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd16_kernel<8>",
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, 8>",
                      "flop_per_launch": attn_flop, "avg_launch_ms": round(avg["attn_fwd"], 4)},
         "phases_ms": {k_: round(x, 4) for k_, x in avg.items()},
         "hbm_GBps": {**{k_: round(phase_bytes[k_] / (avg[k_] * 1e-3) / 1e9, 1)

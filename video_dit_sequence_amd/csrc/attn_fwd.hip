@@ -2,7 +2,8 @@
 // sequence-parallel rank's heads (LTX-2 "Sequence Parallelism (SP)" page:
 // after the head exchange each rank runs global attention over every token
 // for its heads; padded keys are masked out).  bf16 inputs, bf16 matrix-core
-// products with fp32 accumulation, fp32 online softmax.
+// products with fp32 accumulation, fp32 online softmax.  Head dimensions 64
+// and 128.
 //
 // Work split.  One workgroup = W waves = 32 W query rows of one (batch,
 // head); each wave owns 32 query rows for the whole key loop.  At least two
@@ -10,37 +11,42 @@
 // matrix instructions execute.  D = 128 uses 8-wave workgroups (256
 // registers per lane: one workgroup per CU, two waves per SIMD); D = 64 uses
 // 4-wave workgroups held to 168 registers, three per CU, which overlap each
-// other's start and end (the D = 64 workloads have short key loops).
-// attn_fwd_kernel below is the D = 64 kernel, on 32x32x16 products;
-// attn_fwd16_kernel, further down, is the D = 128 one, on 16x16x32 products
-// (same structure; its own comment gives the lane layout).  Keys
+// other's start and end (the D = 64 workloads have short key loops).  Keys
 // stream through LDS in tiles of 64 keys, double-buffered: while tile i is
 // consumed, tile i+1 is copied global -> LDS directly (buffer_load ... lds,
 // no register staging).
 //
-// Matrix-core orientation.  v_mfma_f32_32x32x16_bf16 computes a 32x32 fp32
-// tile C += A(32x16) * B(16x32).  Lane l supplies row (l % 32) of A and
-// column (l % 32) of B, each as 8 consecutive k values starting at
-// 8 * (l / 32); it receives column (l % 32) of C, rows
-// 8 * (r / 4) + 4 * (l / 32) + (r % 4) in accumulator register r.
-// The kernel computes the transposed score tile S^T = K * Q^T (A = 32 keys,
-// B = 32 queries), so every lane holds 16 scores of ONE query: the softmax
-// row statistics are in-register plus one exchange between the two
-// half-waves (ds_bpermute).  The output is accumulated transposed too,
-// O^T = V^T * P^T (A = 32 channels of V^T, B = P^T), so the per-query
-// rescale is a per-lane scalar.
+// Matrix instruction.  The products run on v_mfma_f32_16x16x32_bf16.
+// Measured on MI355X with random bf16 operands, it sustains 15 % more
+// TFLOP/s than v_mfma_f32_32x32x16_bf16 (2088 against 1818, two waves per
+// SIMD).  The reason is power, not issue: the chip lowers its clock under
+// matrix load, and this form draws less per flop.  A 32-head 32768-token
+// launch at D = 128 held 1.97 GHz instead of ~1.7, at ~14 % more cycles:
+// the instruction count doubles, and a wave issuing these products alone
+// leaves gaps.  The cross-attention launch at D = 64 gained 2-5 %.
 //
-// P^T comes straight from the S^T accumulator: for the 16 keys held in
-// registers 8j..8j+7 of a 32-key tile, lane half hf holds keys
-// {4hf..4hf+3, 8+4hf..8+4hf+3} as its k values 0..7.  The V^T operand is read
-// in exactly that key order with two ds_read_b64_tr_b16, which transpose 4
-// rows x 16 columns of 16-bit values across each 16-lane group: lane j of a
-// group receives element j of each of the 4 rows.
+// Lane layout.  Lane l = 16 g + j (g = l / 16) supplies row j of A and
+// column j of B, each as 8 k values of k-slice g, and receives column j of
+// C, rows 4 g + r in accumulator register r.  The kernel computes the
+// transposed score tile S^T = K * Q^T (A = keys, B = queries), so all of a
+// lane's scores belong to its queries, and accumulates O^T = V^T * P^T, so
+// the per-query rescale is a per-lane scalar.  Per wave: 32 queries as two
+// 16-query blocks qb; per 64-key tile, four 16-key blocks kb.  The S^T block
+// (kb, qb) leaves lane l with query 16 qb + j and keys 16 kb + 4 g + r.
+// P^T for the 32-key chunk kc and block qb is the accumulators of key blocks
+// 2 kc and 2 kc + 1, as k values 0..3 and 4..7 of slice g: keys
+// {32 kc + 4 g + r, 32 kc + 16 + 4 g + r}, with no lane exchange.  The V^T
+// operand is read in exactly that key order with two ds_read_b64_tr_b16,
+// which transpose 4 rows x 16 columns of 16-bit values across each 16-lane
+// group: lane j of a group receives element j of each of the 4 rows.  A
+// query's 64 keys of a tile sit in the four lanes j, 16 + j, 32 + j,
+// 48 + j, so its row statistics take two exchanges (needed only for the
+// first tile, a rescale and the final sum).
 //
 // LDS layout.  K and V tiles are row-major [64 keys][D] with the 16-byte
-// chunks of row r permuted by XOR with a function of r (swz64 here; swz_k16
-// and swz_v16 for the head-dimension-128 kernel), so that the rows read by
-// one K fragment or one V transpose read fall in different banks.
+// chunks of row r permuted by XOR with a function of r (swz_k, swz_v), so
+// that the rows read by one K fragment or one V transpose read fall in
+// different banks.
 //
 // Softmax.  Q is pre-multiplied by scale * log2(e) (rounded to bf16 once;
 // or it arrives so multiplied, from the rotary pack, and is used as given),
@@ -49,14 +55,15 @@
 // m is the first tile's row max and is not tracked per tile: the softmax is
 // invariant to the offset, and fp32/bf16 hold probabilities up to 2^127, so
 // m only has to rise when a probability could leave the safe range.  After
-// each tile's exponentials the lane's row sum is checked: at or above 2^64,
-// or not finite, the tile's exact max becomes m, O and the sum are rescaled
-// and the tile's probabilities recomputed.  With the guard at 2^64,
+// each tile's exponentials the lane's row sums are checked: at or above
+// 2^64, or not finite, the tile's exact max becomes m, O and the sums are
+// rescaled and the tile's probabilities recomputed.  With the guard at 2^64,
 // P <= 2^64, O <= 2^64 * |v| * keys and the sum stay far inside fp32.  The
-// probabilities feed the P*V product rounded to bf16; the row sum adds them
-// unrounded in fp32.  The guard tests the sum's bit pattern as an integer, so that a
-// NaN or infinite sum (from non-finite valid inputs) takes the same path on
-// any floating-point compile flags; such rows then come out non-finite.
+// probabilities feed the P*V product rounded to bf16; the row sums add them
+// unrounded in fp32.  The guard tests the sums' bit patterns as integers, so
+// that a NaN or infinite sum (from non-finite valid inputs) takes the same
+// path on any floating-point compile flags; such rows then come out
+// non-finite.
 //
 // Output.  Staged per wave through LDS and stored as whole rows (see the
 // end of the kernel); the row addressing also lets the output land directly
@@ -103,26 +110,42 @@ struct Int {
   static constexpr int value = N;
 };
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Value of x held by lane l ^ 32 (the other half-wave, which holds the other
-// keys of the same query), through the LDS crossbar.
-__device__ __forceinline__ float partner(float x) {
-  const int addr = ((__lane_id() ^ 32) << 2);
+// Value of x held by lane l ^ mask, through the LDS crossbar.
+__device__ __forceinline__ float xlane(float x, int mask) {
+  const int addr = ((__lane_id() ^ mask) << 2);
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
 
-// Chunk permutation of LDS row r (16-byte chunks) for head dimension 64:
-// 8 chunks per 128-byte row, two rows per 256-byte bank window, so a chunk's
-// bank group is 8 (r & 1) + its position.  The permutation takes each half
-// (even rows, odd rows) of r..r+15 to 8 distinct positions (K fragment
-// reads), and gives rows r and r + 2 of a V transpose read permutations that
-// differ in bit 2, so that their chunks 0..3 (or 4..7) fall in disjoint bank
-// groups.  The earlier choice let those rows collide: 1.34e7 conflict cycles
-// per cross-attention launch, now 7.9e5.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 2) & 3) | (((r >> 1) & 1) << 2); }
+// Chunk permutations of the K and V tiles: chunk c of row r is stored at
+// position c ^ swz(r).  A K fragment read gives lane 16 g + j row j (mod 16)
+// and chunk 4 s + g.  A V transpose read is served one 32-lane half at a
+// time over the 64 four-byte banks; the half reads 8 consecutive rows, 8
+// bytes of each of two adjacent chunks {2a, 2a + 1} per row.  Each choice
+// below was measured with SQ_LDS_BANK_CONFLICT on MI355X: zero conflict
+// cycles for both reads.
+// - D = 128 (16 chunks per 256-byte row, one row per bank window): K needs
+//   r % 16.  V needs each 8-row half to spread its chunk pairs over all 64
+//   banks: swz_v sends the pair {2a, 2a + 1} of row r to the position pair
+//   a ^ (r % 8).  Neither works for the other read: one permutation shared
+//   by both tiles costs 4 conflict cycles per K read or 2 per V read (128 per
+//   wave and tile with the earlier shared choice, 4 % of the 32-head
+//   32768-token launch).
+// - D = 64 (8 chunks per 128-byte row, two rows per bank window): r % 8
+//   serves both reads.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : (r & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (r & 7);
+}
 
 // One 16-byte-per-lane copy global -> LDS through buffer resource r: lane l
 // reads byte offset voff and writes LDS bytes [dst + 16 l, +16).  (Kept out
@@ -160,11 +183,11 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
     __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
     int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
     int32_t out_heads) {
-  static_assert(D == 64, "head dimension 128 runs on attn_fwd16_kernel");
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
   constexpr int kThreads = W * 64;
   constexpr int kBQ = W * kQW;          // query rows per workgroup
-  constexpr int KS = D / 16;            // 16-channel steps of K Q^T
-  constexpr int DB = D / 32;            // 32-channel blocks of O^T
+  constexpr int KS = D / 32;            // 32-channel steps of K Q^T
+  constexpr int CB = D / 16;            // 16-channel blocks of O^T
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROW = D * 2;            // bytes per K/V row
   constexpr int TILE = kBK * ROW;       // bytes per K or V tile
@@ -178,13 +201,13 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
 
   const int lid = xcd_contiguous(blockIdx.x, nblocks);
   const int bh = lid / qblocks;
-  const int qb = lid - bh * qblocks;
+  const int qb0 = lid - bh * qblocks;
   const int64_t b = bh / heads;
   const int64_t h = bh - b * heads;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int ln = lane & 31, hf = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
   const int64_t rs = int64_t(heads) * D;  // elements between consecutive tokens
   const __bf16* qbase = q + (b * nq * heads + h) * D;
   const __bf16* kbase = k + (b * nk_pad * heads + h) * D;
@@ -201,395 +224,23 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   asm volatile("" : "+s"(obase), "+s"(lbase));
   const int64_t ors = int64_t(out_heads) * D;  // elements between output tokens
 
-  // Tile copy: DMA instruction j of this wave fills LDS bytes
-  // [(wave*LOADS + j) * 1024, +1024); lane l writes 16-byte slot
-  // s = (wave*LOADS + j)*64 + l = (row s / CH, position s % CH), which holds
-  // the row's global chunk (position ^ swz(row)).  The copy goes through a
-  // buffer resource whose extent ends with the last valid key: rows past it
-  // read as zeros, so the padded keys are never touched.
   const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
   const int full_tiles = static_cast<int>(nk_valid / kBK);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t cp_off[LOADS];
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int s = (wave * LOADS + j) * 64 + lane;
-    const int row = s / CH;
-    cp_off[j] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz64(row)) * 8) * 2);
-  }
-  auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
-    const int64_t first = int64_t(t) * kBK;
-    const int64_t rows = nk_valid - first < kBK ? nk_valid - first : kBK;
-    const uint32_t extent = static_cast<uint32_t>((rows - 1) * rs * 2 + D * 2);
-    const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbase + first * rs, extent);
-    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbase + first * rs, extent);
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      LDS_AS void* kd = (LDS_AS void*)(dK + (wave_u * LOADS + j) * 1024);
-      LDS_AS void* vd = (LDS_AS void*)(dV + (wave_u * LOADS + j) * 1024);
-      dma16(rk, kd, cp_off[j]);
-      dma16(rv, vd, cp_off[j]);
-    }
-  };
-
-  // Bytes a copy leaves unwritten must not hold stale NaN patterns (a V row
-  // past nk_valid meets a zero probability, and 0 * NaN is NaN): each lane
-  // first zeroes the 16-byte slots its own copies fill, in every stage, and
-  // waits for those stores before its first copy, so no ordering between
-  // waves is needed.  Tile 0 is then requested before Q is read, so that
-  // the two loads' latencies overlap.
-  {
-    char* const ring[4] = {sK0, sK1, sV0, sV1};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j)
-        *reinterpret_cast<u32x4*>(ring[i] + (wave * LOADS + j) * 1024 + lane * 16) = u32x4{};
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  }
-  issue_tile(0, sK0, sV0);
-
-  // Q^T operand: query row q0 + ln, channels 16*s + 8*hf .. +7.
-  const int64_t qrow = int64_t(qb) * kBQ + wave * kQW + ln;
-  // Q is multiplied by scale * log2(e) once here (rounded back to bf16), so
-  // that the products are already log2-domain scores.  (For log2-domain q
-  // the factor is 1.0f, and the value passes through unchanged.)
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    bf16x8 x = qrow < nq ? *reinterpret_cast<const bf16x8*>(qbase + qrow * rs + s * 16 + hf * 8) : bf16x8{};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * scale_log2);
-    qf[s] = x;
-  }
-
-  // Per-lane LDS offsets inside a tile.
-  // K fragment (S^T A operand) for step s: row ln (+32 for the second key
-  // block), chunk 2s + hf, stored at position (2s + hf) ^ swz(ln).
-  // V fragment for channel block d: two transpose reads; 16-lane group g,
-  // index gi inside it; rows 16G + 8r + 4(g/2) + gi/4, channels
-  // 32d + 16(g%2) + 4(gi%4).
-  int k_off[KS], v_off0[DB], v_off1[DB];
-  {
-    const int k_x = hf ^ swz64(ln);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) k_off[s] = ln * ROW + (((2 * s) ^ k_x) << 4);
-    const int g = lane >> 4, gi = lane & 15;
-    const int v_row0 = 4 * (g >> 1) + (gi >> 2);
-    const int v_c = 2 * (g & 1) + ((gi & 3) >> 1);
-    const int v_x0 = v_c ^ swz64(v_row0);
-    const int v_x1 = v_c ^ swz64(v_row0 + 8);
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      v_off0[d] = v_row0 * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x0) << 4);
-      v_off1[d] = (v_row0 + 8) * ROW + (gi & 1) * 8 + (((d * 4) ^ v_x1) << 4);
-    }
-  }
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
-  // Softmax state.  m is the offset subtracted from every log2-domain score
-  // before exp2: the first tile's max, raised only by the sum guard.  The
-  // score products start from a register block holding -m, so they come out
-  // already offset (no per-score VALU).
-  float m = 0.0f;       // replaced by the first tile's max
-  float l = 0.0f;       // running sum over this lane's keys
-  f32x16 neg_m = f32x16{};
-
-  auto compute_tile = [&] __device__(int t, const char* cK, const char* cV, auto masked, auto first)
-                          __attribute__((always_inline)) {
-    const LDS_AS char* lK = (const LDS_AS char*)cK;
-    const LDS_AS char* lV = (const LDS_AS char*)cV;
-    // Keep the stage base out of the per-lane offsets (it is folded into
-    // each read's immediate offset instead of costing a register per stage).
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(k_off[s]));
-#pragma unroll
-    for (int d = 0; d < DB; ++d) asm volatile("" : "+v"(v_off0[d]), "+v"(v_off1[d]));
-    // S^T = K * Q^T for the two 32-key blocks of the tile.  Fragment i feeds
-    // block i % 2 at channel step i / 2, so consecutive products are
-    // independent; reads run kKAhead fragments ahead of the products.
-    f32x16 sc[2] = {neg_m, neg_m};
-    // Matrix sections run at raised wave priority: when the other wave on
-    // this SIMD is in its softmax, its vector instructions fill the cycles
-    // between these products instead of delaying them.
-    __builtin_amdgcn_s_setprio(1);
-    {
-      bf16x8 kf[2 * KS];
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i)
-        kf[i] = *(const LDS_AS bf16x8*)(lK + (i & 1) * 32 * ROW + k_off[i >> 1]);
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) sc[i & 1] = mfma32(kf[i], qf[i >> 1], sc[i & 1]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKAhead, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * KS - kKAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKAhead, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
-    if constexpr (decltype(masked)::value != 0) {
-      // Key of register r in block kb is 32kb + 8(r/4) + 4hf + r%4: compare
-      // its lane-independent part against the lane's limit.
-      const int lim = static_cast<int>(nk_valid - int64_t(t) * kBK) - 4 * hf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
-    }
-    auto tile_max = [&] __device__() __attribute__((always_inline)) {
-      float a = fmaxf(sc[0][0], sc[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sc[0][r]), sc[1][r]);
-      return fmaxf(a, partner(a));  // tile max, relative to m
-    };
-    auto shift = [&] __device__(float delta) __attribute__((always_inline)) {
-      m += delta;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[0][r] -= delta;
-        sc[1][r] -= delta;
-        neg_m[r] = -m;
-      }
-    };
-    if constexpr (decltype(first)::value != 0) shift(tile_max());   // the first tile sets m to its max
-    float sum = 0.0f;
-    bf16x8 pf[4];
-    // Probabilities: exp2 of the offset scores, rounded to bf16 for the P*V
-    // product.  The lane's row sum adds the unrounded fp32 values with plain
-    // adds, in two chains (even and odd keys) added at the end.  Measured on
-    // MI355X: v_dot2c_f32_bf16 (which would sum the bf16 values) does not
-    // overlap the matrix instructions while fp32 adds do; the adds are +2 %
-    // on the 32-head 32768-token launch over two dot-product chains, which
-    // were +2 % over one.
-    auto probs = [&] __device__() __attribute__((always_inline)) {
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        const int kb = G >> 1, j = G & 1;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e]);
-          const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * j + e + 1]);
-          pf[G][e] = static_cast<__bf16>(p0);
-          pf[G][e + 1] = static_cast<__bf16>(p1);
-          s0 += p0;
-          s1 += p1;
-        }
-      }
-      sum = s0 + s1;
-    };
-    probs();
-    // m is only raised when a probability could leave the safe range (a
-    // lane's sum at or above 2^64, +inf or NaN: with the sign bit cleared,
-    // exactly the patterns that compare at or above kSumGuardBits as
-    // unsigned integers).  Then the tile's exact max becomes the new m, the
-    // accumulated state is rescaled and the probabilities are recomputed;
-    // P*V has not consumed them yet.
-    if (__builtin_amdgcn_ballot_w64((__builtin_bit_cast(uint32_t, sum) & 0x7fffffffu) >= kSumGuardBits)) {
-      const float delta = fmaxf(tile_max(), 0.0f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-      shift(delta);
-      probs();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    bf16x8 vf[4 * DB];
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      const int G = i / DB, d = i % DB;
-      vf[i] = lds_tr_pair(lV + G * 16 * ROW + v_off0[d], lV + G * 16 * ROW + v_off1[d]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) acc[i % DB] = mfma32(vf[i], pf[i / DB], acc[i % DB]);
-    l += sum;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVAhead, 1);
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-      if (i + kVAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  char* const ringK[kStages] = {sK0, sK1};
-  char* const ringV[kStages] = {sV0, sV1};
-
-  // One iteration with the ring slot known at compile time: wait for tile t
-  // (stage ST), then copy tile t+1 into the other stage (which held tile
-  // t-1: every wave is done with it once past the barrier) and consume tile t.
-  auto iteration = [&] __device__(int t, auto st, auto masked, auto first) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    constexpr int S1 = (ST + 1) % kStages;
-    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);  // this thread's copies of tile t landed
-    __syncthreads();                         // everyone's
-    if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
-    compute_tile(t, ringK[ST], ringV[ST], masked, first);
-  };
-
-  // Tile 0, which sets the offset m, runs outside the loop: with the
-  // first-tile branch in the loop, the register allocator copied the -m block
-  // with 64-bit moves on every tile (peeled: +1.7 % on the 32-head
-  // 32768-token launch).  Then pairs of wholly valid tiles, no masking; then
-  // at most one more full tile and the one tile that straddles nk_valid.
-  if (full_tiles >= 1)
-    iteration(0, Int<0>{}, Int<0>{}, Int<1>{});
-  else
-    iteration(0, Int<0>{}, Int<1>{}, Int<1>{});
-  int t = 1;
-  for (; t + 2 <= full_tiles; t += 2) {
-    iteration(t, Int<1>{}, Int<0>{}, Int<0>{});
-    iteration(t + 1, Int<0>{}, Int<0>{}, Int<0>{});
-  }
-  if (t < full_tiles) {
-    iteration(t, Int<1>{}, Int<0>{}, Int<0>{});
-    if (t + 1 < ntiles) iteration(t + 1, Int<0>{}, Int<1>{}, Int<0>{});
-  } else if (t < ntiles) {
-    iteration(t, Int<1>{}, Int<1>{}, Int<0>{});
-  }
-
-  const float lt = l + partner(l);
-  const float inv = 1.0f / lt;
-  if (lbase && hf == 0 && qrow < nq) lbase[qrow] = (m + __builtin_log2f(lt)) * 0.69314718055994531f;
-
-  // Output.  A lane holds 4-channel pieces of one query row, so storing
-  // them directly would scatter 8-byte writes over 32 rows per instruction;
-  // with a wide token stride (the unpacked layout) the L2 then writes lines
-  // back half-filled.  Instead each wave stages its 32 x D tile in LDS (the
-  // ring is free once every wave has left the key loop), row-major with the
-  // 16-byte chunks of row r permuted by XOR with r % CH, and writes whole
-  // rows: 16 bytes per lane, 64 / CH rows per instruction.
-  static_assert(2 * kQW == kBK && W <= 8, "two waves' output tiles fill one ring stage");
-  __syncthreads();
-  char* const stage = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sV0 : sV1) + (wave & 1) * (kQW * ROW);
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const u32x2 w = {pack_bf16x2(acc[d][4 * rg] * inv, acc[d][4 * rg + 1] * inv),
-                       pack_bf16x2(acc[d][4 * rg + 2] * inv, acc[d][4 * rg + 3] * inv)};
-      const int c = 4 * d + rg;  // 16-byte chunk: channels 8c .. 8c + 7; this half holds 4hf .. 4hf + 3
-      *reinterpret_cast<u32x2*>(stage + ln * ROW + ((c ^ (ln % CH)) << 4) + hf * 8) = w;
-    }
-  __syncthreads();
-  constexpr int RPI = 64 / CH;  // rows per store instruction
-  const int64_t q0 = int64_t(qb) * kBQ + wave * kQW;
-#pragma unroll
-  for (int i = 0; i < kQW / RPI; ++i) {
-    const int r = i * RPI + lane / CH, c = lane % CH;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * ROW + ((c ^ (r % CH)) << 4));
-    if (q0 + r < nq) *reinterpret_cast<u32x4*>(obase + (q0 + r) * ors + c * 8) = w;
-  }
-}
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// Value of x held by lane l ^ mask, through the LDS crossbar.
-__device__ __forceinline__ float xlane(float x, int mask) {
-  const int addr = ((__lane_id() ^ mask) << 2);
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
-}
-
-// Chunk permutations of the K and V tiles for head dimension 128 (16 chunks
-// of 16 bytes per 256-byte row), one per tensor because the two fragment
-// reads of attn_fwd16_kernel need different ones.  Chunk c of row r is
-// stored at position c ^ swz(r).
-// - K: a fragment read gives lane 16 g + j row j (mod 16), chunk 4 s + g.
-//   With position c ^ (r % 16) these 128-bit reads run without bank
-//   conflicts (measured with SQ_LDS_BANK_CONFLICT on MI355X).
-// - V: a transpose read is served one 32-lane half at a time, over the 64
-//   four-byte banks.  A half reads 8 consecutive rows (0..7 or 8..15 mod 16),
-//   8 bytes of each of two adjacent chunks {2a, 2a + 1} per row.  swz_v16
-//   sends that chunk pair of row r to the position pair a ^ (r % 8), so the 8
-//   rows cover all 64 banks once.
-// One permutation shared by both tiles (the 32x32x16 kernel's) cost 4
-// conflict cycles per K read and 2 per V read here: 128 per wave and tile,
-// and 4 % of the 32-head 32768-token launch.
-__device__ __forceinline__ int swz_k16(int r) { return r & 15; }
-__device__ __forceinline__ int swz_v16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-// Head dimension 128: the same tiling, ring, softmax and output staging as
-// attn_fwd_kernel, with the products on v_mfma_f32_16x16x32_bf16.  Measured on
-// MI355X, that instruction sustains 15 % more TFLOP/s than the 32x32x16 one
-// on random operands (the clock falls less under its power draw: a 32-head
-// 32768-token launch ran at 2.0 GHz instead of 1.7), at the cost of twice the
-// matrix instructions (~16 % more cycles in this kernel); the net gain on
-// that launch is 0.5-2.4 % box to box, 2-4 % on shorter key loops.
-//
-// Lane l = 16 g + j (g = l / 16) supplies row j of A and column j of B, each
-// as 8 k values of k-slice g, and receives column j of C, rows 4 g + r in
-// accumulator register r.  Per wave: 32 queries as two 16-query blocks qb;
-// per 64-key tile, four 16-key blocks kb.  The S^T block (kb, qb) =
-// K[16 kb .. 16 kb + 15] * Q^T[qb] leaves lane l with query 16 qb + j and keys
-// 16 kb + 4 g + r.  P^T for the 32-key chunk kc and block qb is those of key
-// blocks 2 kc and 2 kc + 1, as k values 0..3 and 4..7 of slice g: keys
-// {32 kc + 4 g + r, 32 kc + 16 + 4 g + r}, straight from the accumulators; V^T
-// is read in the same key order with two transpose reads per fragment.  A
-// query's 64 keys of a tile sit in the four lanes j, 16 + j, 32 + j, 48 + j,
-// so its row statistics take two exchanges (only for the first tile, a
-// rescale and the final sum).
-template <int W>
-__global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int64_t nq, int64_t nk_pad, int64_t nk_valid,
-    int32_t heads, int32_t qblocks, int32_t nblocks, float scale_log2, int32_t out_batch,
-    int32_t out_heads) {
-  constexpr int D = 128;
-  constexpr int kThreads = W * 64;
-  constexpr int kBQ = W * kQW;          // query rows per workgroup
-  constexpr int KS = D / 32;            // 32-channel steps of K Q^T
-  constexpr int CB = D / 16;            // 16-channel blocks of O^T
-  constexpr int CH = D / 8;             // 16-byte chunks per row
-  constexpr int ROW = D * 2;            // bytes per K/V row
-  constexpr int TILE = kBK * ROW;       // bytes per K or V tile
-  constexpr int LOADS = TILE / (kThreads * 16);
-  static_assert(LOADS * kThreads * 16 == TILE, "tile copy covers the tile");
-
-  __shared__ __attribute__((aligned(1024))) char sK0[TILE], sK1[TILE];
-  __shared__ __attribute__((aligned(1024))) char sV0[TILE], sV1[TILE];
-
-  const int lid = xcd_contiguous(blockIdx.x, nblocks);
-  const int bh = lid / qblocks;
-  const int qb0 = lid - bh * qblocks;
-  const int64_t b = bh / heads;
-  const int64_t h = bh - b * heads;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, j = lane & 15;
-  const int64_t rs = int64_t(heads) * D;
-  const __bf16* qbase = q + (b * nq * heads + h) * D;
-  const __bf16* kbase = k + (b * nk_pad * heads + h) * D;
-  const __bf16* vbase = v + (b * nk_pad * heads + h) * D;
-  const int32_t ob = static_cast<int32_t>(b) % out_batch, op = static_cast<int32_t>(b) / out_batch;
-  __bf16* obase = o + ((int64_t(ob) * nq * out_heads) + int64_t(op) * heads + h) * D;
-  float* lbase = lse ? lse + (b * heads + h) * nq : nullptr;
-  asm volatile("" : "+s"(obase), "+s"(lbase));
-  const int64_t ors = int64_t(out_heads) * D;
-
-  const int ntiles = static_cast<int>((nk_valid + kBK - 1) / kBK);
-  const int full_tiles = static_cast<int>(nk_valid / kBK);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // Tile copy as in attn_fwd_kernel; K and V tiles take different chunk
-  // permutations (swz_k16, swz_v16), so each lane has a source offset per tensor.
+  // Tile copy: DMA instruction i of this wave fills LDS bytes
+  // [(wave*LOADS + i) * 1024, +1024); lane l writes 16-byte slot
+  // s = (wave*LOADS + i)*64 + l = (row s / CH, position s % CH), which holds
+  // the row's global chunk (position ^ swz(row)); K and V take different
+  // permutations, so each lane has a source offset per tensor.  The copy goes
+  // through a buffer resource whose extent ends with the last valid key: rows
+  // past it read as zeros, so the padded keys are never touched.
   uint32_t cpk_off[LOADS], cpv_off[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int s = (wave * LOADS + i) * 64 + lane;
     const int row = s / CH;
-    cpk_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_k16(row)) * 8) * 2);
-    cpv_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_v16(row)) * 8) * 2);
+    cpk_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_k<D>(row)) * 8) * 2);
+    cpv_off[i] = static_cast<uint32_t>((row * rs + ((s % CH) ^ swz_v<D>(row)) * 8) * 2);
   }
   auto issue_tile = [&] __device__(int t, char* dK, char* dV) __attribute__((always_inline)) {
     const int64_t first = int64_t(t) * kBK;
@@ -605,6 +256,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
       dma16(rv, vd, cpv_off[i]);
     }
   };
+  // Bytes a copy leaves unwritten must not hold stale NaN patterns (a V row
+  // past nk_valid meets a zero probability, and 0 * NaN is NaN): each lane
+  // first zeroes the 16-byte slots its own copies fill, in every stage, and
+  // waits for those stores before its first copy, so no ordering between
+  // waves is needed.  Tile 0 is then requested before Q is read, so that
+  // the two loads' latencies overlap.
   {
     char* const ring[4] = {sK0, sK1, sV0, sV1};
 #pragma unroll
@@ -617,6 +274,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
   issue_tile(0, sK0, sV0);
 
   // Q^T operands: block qb holds query row q0 + 32 wave + 16 qb + j, channels 32 s + 8 g .. +7.
+  // Q is multiplied by scale * log2(e) once here (rounded back to bf16), so
+  // that the products are already log2-domain scores.  (For log2-domain q
+  // the factor is 1.0f, and the value passes through unchanged.)
   const int64_t qrow0 = int64_t(qb0) * kBQ + wave * kQW + j;
   bf16x8 qf[2][KS];
 #pragma unroll
@@ -632,15 +292,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
   }
 
   // LDS offsets.  K fragment (A of S^T) for key block kb, step s: row 16 kb + j, chunk 4 s + g
-  // at position (4 s + g) ^ swz_k16(row), which depends on row % 16 = j.  V fragment (A of
+  // at position (4 s + g) ^ swz_k(row), which depends on row % 16 = j.  V fragment (A of
   // O^T) for channel block cb, key chunk kc: transpose reads of rows 32 kc + 4 g + j / 4 (and
   // + 16), columns 16 cb + 4 (j % 4); row % 16 = 4 g + j / 4 for all of them.
   int k_off[KS], v_off[CB];
   {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) k_off[s] = j * ROW + (((4 * s + g) ^ swz_k16(j)) << 4);
+    for (int s = 0; s < KS; ++s) k_off[s] = j * ROW + (((4 * s + g) ^ swz_k<D>(j)) << 4);
     const int vr = 4 * g + (j >> 2);
-    const int vs = swz_v16(vr);
+    const int vs = swz_v<D>(vr);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       v_off[cb] = vr * ROW + (j & 1) * 8 + (((2 * cb + ((j & 3) >> 1)) ^ vs) << 4);
@@ -649,6 +309,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
   f32x4 acc[CB][2];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{};
+  // Softmax state of the two queries of each lane.  m is the offset
+  // subtracted from every log2-domain score before exp2: the first tile's
+  // max, raised only by the sum guard.  The score products start from a
+  // register block holding -m, so they come out already offset.  l is the
+  // running sum over this lane's keys.
   float m[2] = {0.0f, 0.0f};
   float l[2] = {0.0f, 0.0f};
   f32x4 neg_m[2] = {f32x4{}, f32x4{}};
@@ -657,6 +322,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
                           __attribute__((always_inline)) {
     const LDS_AS char* lK = (const LDS_AS char*)cK;
     const LDS_AS char* lV = (const LDS_AS char*)cV;
+    // Keep the stage base out of the per-lane offsets (it is folded into
+    // each read's immediate offset instead of costing a register per stage).
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(k_off[s]));
 #pragma unroll
@@ -664,6 +331,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
     f32x4 sc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sc[kb][0] = neg_m[0], sc[kb][1] = neg_m[1];
+    // Matrix sections run at raised wave priority: when the other wave on
+    // this SIMD is in its softmax, its vector instructions fill the cycles
+    // between these products instead of delaying them.  S^T: fragment i
+    // (key block i % 4, channel step i / 4) feeds both query blocks; reads
+    // run kKAhead fragments ahead of the products.
     __builtin_amdgcn_s_setprio(1);
     {
       bf16x8 kf[4 * KS];
@@ -720,6 +392,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
       }
     };
     if constexpr (decltype(first)::value != 0) shift(tile_max(0), tile_max(1));
+    // Probabilities: exp2 of the offset scores, rounded to bf16 for the P*V
+    // product.  The row sums add the unrounded fp32 values with plain adds.
+    // (Measured on MI355X: v_dot2c_f32_bf16, which would sum the bf16
+    // values, does not overlap the matrix instructions, while fp32 adds do.)
     float sum0 = 0.0f, sum1 = 0.0f;
     bf16x8 pf[2][2];
     auto probs = [&] __device__() __attribute__((always_inline)) {
@@ -745,6 +421,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
       sum1 = s1;
     };
     probs();
+    // m is only raised when a probability could leave the safe range (a
+    // lane's sum at or above 2^64, +inf or NaN: with the sign bit cleared,
+    // exactly the patterns that compare at or above kSumGuardBits as
+    // unsigned integers).  Then the tile's exact max becomes the new m, the
+    // accumulated state is rescaled and the probabilities are recomputed;
+    // P*V has not consumed them yet.
     const uint32_t worst = (__builtin_bit_cast(uint32_t, sum0) & 0x7fffffffu) >
                                    (__builtin_bit_cast(uint32_t, sum1) & 0x7fffffffu)
                                ? (__builtin_bit_cast(uint32_t, sum0) & 0x7fffffffu)
@@ -790,14 +472,21 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
 
   char* const ringK[kStages] = {sK0, sK1};
   char* const ringV[kStages] = {sV0, sV1};
+  // One iteration with the ring slot known at compile time: wait for tile t
+  // (stage ST), then copy tile t+1 into the other stage (which held tile
+  // t-1: every wave is done with it once past the barrier) and consume tile t.
   auto iteration = [&] __device__(int t, auto st, auto masked, auto first) __attribute__((always_inline)) {
     constexpr int ST = decltype(st)::value;
     constexpr int S1 = (ST + 1) % kStages;
-    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);  // this thread's copies of tile t landed
+    __syncthreads();                         // everyone's
     if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
     compute_tile(t, ringK[ST], ringV[ST], masked, first);
   };
+  // Tile 0, which sets the offset m, runs outside the loop (with the
+  // first-tile branch in the loop, the register allocator copied the -m
+  // block on every tile).  Then pairs of wholly valid tiles, no masking; then
+  // at most one more full tile and the one tile that straddles nk_valid.
   if (full_tiles >= 1)
     iteration(0, Int<0>{}, Int<0>{}, Int<1>{});
   else
@@ -827,6 +516,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
       if (qrow0 + 16 * qb < nq) lbase[qrow0 + 16 * qb] = (m[qb] + __builtin_log2f(lt[qb])) * 0.69314718055994531f;
   }
 
+  // Output.  A lane holds 4-channel pieces of its query rows, so storing them
+  // directly would scatter 8-byte writes over 16 rows per instruction; with
+  // a wide token stride (the unpacked layout) the L2 then writes lines back
+  // half-filled.  Instead each wave stages its 32 x D tile in LDS (the ring
+  // is free once every wave has left the key loop), row-major with the
+  // 16-byte chunks of row r permuted by XOR with r % CH, and writes whole
+  // rows: 16 bytes per lane, 64 / CH rows per instruction.
   static_assert(2 * kQW == kBK && W <= 8, "two waves' output tiles fill one ring stage");
   __syncthreads();
   char* const stage = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sV0 : sV1) + (wave & 1) * (kQW * ROW);
@@ -844,7 +540,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd16_kernel(
     }
   }
   __syncthreads();
-  constexpr int RPI = 64 / CH;
+  constexpr int RPI = 64 / CH;  // rows per store instruction
   const int64_t q0 = int64_t(qb0) * kBQ + wave * kQW;
 #pragma unroll
   for (int i = 0; i < kQW / RPI; ++i) {
@@ -869,13 +565,7 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Log2-domain q is taken as given: x * 1.0f rounded to bf16 is x.
   const float scale_log2 = q_log2 ? 1.0f : static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  auto kernel = [] {
-    if constexpr (D == 128)
-      return attn_fwd16_kernel<W>;
-    else
-      return attn_fwd_kernel<D, W>;
-  }();
-  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, W>), dim3(static_cast<uint32_t>(nblocks)), dim3(W * 64), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nq, nk_pad, nk_valid,
                      heads, static_cast<int32_t>(qblocks), static_cast<int32_t>(nblocks), scale_log2,
