@@ -97,11 +97,10 @@ constexpr int kVAhead = 3;        // V fragments in flight ahead of the products
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // chips: 32-bit data format, everything else zero.
 constexpr int kBufferFlags = 0x00020000;
-// s_waitcnt immediates for vmcnt(n), n = 0..15, with expcnt and lgkmcnt left
-// at their maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8).
-constexpr short kWaitVm[16] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75, 0x0F76, 0x0F77,
-                               0x0F78, 0x0F79, 0x0F7A, 0x0F7B, 0x0F7C, 0x0F7D, 0x0F7E, 0x0F7F};
+// s_waitcnt immediate for vmcnt(0), with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).
+constexpr short kWaitVm0 = 0x0F70;
 // s_waitcnt immediate for lgkmcnt(0), vmcnt and expcnt at their maxima.
 constexpr short kWaitLgkm0 = static_cast<short>(0xC07F);
 
@@ -478,7 +477,7 @@ __global__ __launch_bounds__(W * 64, min_blocks_for<W>()) void attn_fwd_kernel(
   auto iteration = [&] __device__(int t, auto st, auto masked, auto first) __attribute__((always_inline)) {
     constexpr int ST = decltype(st)::value;
     constexpr int S1 = (ST + 1) % kStages;
-    __builtin_amdgcn_s_waitcnt(kWaitVm[0]);  // this thread's copies of tile t landed
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this thread's copies of tile t landed
     __syncthreads();                         // everyone's
     if (t + 1 < ntiles) issue_tile(t + 1, ringK[S1], ringV[S1]);
     compute_tile(t, ringK[ST], ringV[ST], masked, first);

@@ -9,7 +9,6 @@ namespace ltxa {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Workgroups are dealt to the 8 XCDs of an MI355X round-robin by launch
 // index.  This maps the launch index to a logical index so that each XCD
