@@ -185,6 +185,29 @@ def test_ragged_shapes(nq, nk_pad, nk_valid, D):
     _compare(q, k, v, nk_valid, nq, 1.0 / np.sqrt(D), what=f"shape {nq}x{nk_pad}/{nk_valid} d{D}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_masked_tile_every_tail(D):
+    # Only the tile that straddles nk_valid is masked: each score's key index
+    # inside the tile (16 kb + 4 g + r for register r of key block kb in lane
+    # group g) is compared with the valid count.  Tails of 1..64 keys put
+    # the boundary at every key position, in the first tile (which runs
+    # outside the key loop) and after one whole tile.  The padded keys hold
+    # NaN, so a key read past nk_valid would show.  40 query rows leave a
+    # partly filled query block.
+    g = torch.Generator().manual_seed(4000 + D)
+    nq, nk_pad = 40, 128
+    q = wl.randn_bf16((1, nq, 2, D), g)
+    k = wl.randn_bf16((1, nk_pad, 2, D), g)
+    v = wl.randn_bf16((1, nk_pad, 2, D), g)
+    for base in (0, 64):
+        for tail in range(1, 65):
+            nk = base + tail
+            kp, vp = k.clone(), v.clone()
+            kp[:, nk:] = float("nan")
+            vp[:, nk:] = float("nan")
+            _compare(q, kp, vp, nk, nq, 1.0 / np.sqrt(D), what=f"tail {base}+{tail} d{D}")
+
+
 def test_padded_keys_never_leak_bit_exact():
     # Poisoned padding (NaN and huge values) gives the same bits as zero padding.
     w = wl.WORKLOADS["tiny_231"]
