@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 104 /* major*100 + minor */
+#define LTXA_VERSION 105 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -274,6 +274,56 @@ int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t
                          int32_t axes, const double* max_pos, int64_t batch, int32_t heads,
                          int32_t head_dim, int32_t world_size, double theta,
                          const ltxa_rope_opts* opts, void* stream);
+
+/*
+ * Angle tables.  The FastVideo gemma page computes the rotary frequencies
+ * once (precompute_ltx_freqs_cis) and applies them to each tensor later
+ * (apply_ltx_rotary_emb).  The two calls below split the head-shared grid
+ * the same way: the angles of a position buffer are evaluated once into a
+ * caller-owned table, and every tensor rotated with those positions reads
+ * them.
+ *
+ * ltxa_rope_table -- cos and sin of every (token, pair) of the head-shared
+ * grid.
+ *   pos: DEVICE int32 [n_tokens, axes]; max_pos: HOST array of `axes`
+ *     values; theta: frequency base; head_dim: channels per head.
+ *   opts: NULL or the variants above; only fp64_angles and middle act.
+ *     rope_type does not change a pair's angle.  grid_heads and out_scale
+ *     must be 0: the table serves the head-shared grid, and scaling belongs
+ *     to the rotation.
+ *   table: DEVICE fp32 [n_tokens, head_dim/2, 2] (written, caller-owned):
+ *     table[n][i] = (cos, sin) of pair i's angle for token n, evaluated
+ *     exactly as ltxa_rope_ex evaluates it (1 and 0 for the pairs the
+ *     schedule leaves unrotated).
+ * Errors: E_NULL (pos, max_pos or table NULL); E_SHAPE (as ltxa_rope_ex for
+ * head_dim, axes, max_pos, theta and opts; grid_heads or out_scale not 0);
+ * E_ALIGN (pos or table not 16-byte aligned, or head_dim*2 not a multiple
+ * of 16); E_ALIAS (table overlaps pos); E_RANGE.
+ */
+int ltxa_rope_table(const int32_t* pos, int64_t n_tokens, int32_t axes, const double* max_pos,
+                    int32_t head_dim, double theta, const ltxa_rope_opts* opts, float* table,
+                    void* stream);
+
+/*
+ * ltxa_sp_pack_rope_table -- ltxa_sp_pack_rope_ex with the angles read from
+ * a table of ltxa_rope_table.
+ *   src: bf16 [batch, n_tokens, heads, head_dim], read only.
+ *   dst: bf16 [world_size, batch, n_tokens, heads/world_size, head_dim],
+ *     written.
+ *   table: DEVICE fp32 [n_tokens, head_dim/2, 2], read only.
+ *   rope_type: LTXA_ROPE_INTERLEAVED or LTXA_ROPE_SPLIT.
+ *   out_scale: 0 (none), or finite and > 0, as in ltxa_rope_opts.
+ * dst equals, bit for bit, ltxa_sp_pack_rope_ex with the opts the table was
+ * made with, plus this rope_type and out_scale.
+ * Errors: E_NULL (src, dst or table NULL); E_SHAPE (a size < 1, head_dim
+ * odd or above 256, rope_type not 0/1, out_scale neither 0 nor finite and
+ * > 0); E_DIVISIBILITY (as ltxa_sp_pack); E_ALIGN (src, dst or table not
+ * 16-byte aligned, head_dim*2 not a multiple of 16, or SPLIT with
+ * head_dim % 16 != 0); E_ALIAS (dst overlaps src or table); E_RANGE.
+ */
+int ltxa_sp_pack_rope_table(const void* src, void* dst, const float* table, int64_t n_tokens,
+                            int64_t batch, int32_t heads, int32_t head_dim, int32_t world_size,
+                            int32_t rope_type, float out_scale, void* stream);
 
 /*
  * Log2-domain queries.  The attention computes its softmax in base 2: with

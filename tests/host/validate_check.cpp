@@ -218,6 +218,66 @@ void rope_opts_checks() {
   EXPECT(run(opts(1, 0, 0, 0, 0, 0), 32, 40), LTXA_E_ALIGN);  // split needs head_dim % 16 == 0
 }
 
+void rope_table_checks() {
+  using ltxa::check_pack_rope_table;
+  using ltxa::check_rope_angles;
+  std::vector<double> mp3 = {16.0, 32.0, 64.0};
+  const double* m = mp3.data();
+  auto angles = [&](const ltxa_rope_opts* o, int64_t n = 32768, int32_t axes = 3, int32_t hd = 128,
+                    uintptr_t pos = kC, uintptr_t table = kD) {
+    return check_rope_angles(devpos(pos), n, axes, m, hd, 1e4, o, devf(table));
+  };
+  EXPECT(angles(nullptr), LTXA_OK);
+  EXPECT(check_rope_angles(nullptr, 32768, 3, m, 128, 1e4, nullptr, devf(kD)), LTXA_E_NULL);
+  EXPECT(check_rope_angles(devpos(kC), 32768, 3, nullptr, 128, 1e4, nullptr, devf(kD)), LTXA_E_NULL);
+  EXPECT(check_rope_angles(devpos(kC), 32768, 3, m, 128, 1e4, nullptr, nullptr), LTXA_E_NULL);
+  EXPECT(angles(nullptr, 0), LTXA_E_SHAPE);
+  EXPECT(angles(nullptr, 32768, 4), LTXA_E_SHAPE);
+  EXPECT(angles(nullptr, 32768, 3, 127), LTXA_E_SHAPE);
+  EXPECT(check_rope_angles(devpos(kC), 32768, 3, m, 128, kInf, nullptr, devf(kD)), LTXA_E_SHAPE);
+  EXPECT(angles(nullptr, 32768, 3, 6), LTXA_E_ALIGN);
+  EXPECT(angles(nullptr, 32768, 3, 128, kC, kD + 4), LTXA_E_ALIGN);
+  EXPECT(angles(nullptr, 32768, 3, 128, kC + 4), LTXA_E_ALIGN);
+  {
+    ltxa_rope_opts o1{0, 0, 0, 1, 1, 0.0f}, o2{1, 0, 0, 0, 0, 0.0f}, o3{0, 4, 0, 0, 0, 0.0f},
+        o4{0, 0, 0, 0, 0, 0.5f}, o5{3, 0, 0, 0, 0, 0.0f};
+    EXPECT(angles(&o1), LTXA_OK);  // fp64 angles, cell middles
+    EXPECT(angles(&o2), LTXA_OK);  // split pairing: same angles
+    EXPECT(angles(&o3), LTXA_E_SHAPE);
+    EXPECT(angles(&o4), LTXA_E_SHAPE);
+    EXPECT(angles(&o5), LTXA_E_SHAPE);
+  }
+  EXPECT(angles(nullptr, 32768, 3, 128, kC, kC + 64), LTXA_E_ALIAS);
+  EXPECT(angles(nullptr, int64_t(1) << 33), LTXA_E_RANGE);
+  EXPECT(angles(nullptr, INT64_MAX / 2), LTXA_E_RANGE);
+
+  auto pack = [&](int64_t n, int64_t b, int32_t h, int32_t hd, int32_t p, int32_t type, float sc,
+                  uintptr_t src = kA, uintptr_t dst = kB, uintptr_t table = kD) {
+    return check_pack_rope_table(dev(src), dev(dst), devf(table), n, b, h, hd, p, type, sc);
+  };
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f), LTXA_OK);
+  EXPECT(pack(32768, 1, 32, 128, 8, 1, 0.18033688f), LTXA_OK);
+  EXPECT(check_pack_rope_table(nullptr, dev(kB), devf(kD), 32768, 1, 32, 128, 8, 0, 0.0f), LTXA_E_NULL);
+  EXPECT(check_pack_rope_table(dev(kA), nullptr, devf(kD), 32768, 1, 32, 128, 8, 0, 0.0f), LTXA_E_NULL);
+  EXPECT(check_pack_rope_table(dev(kA), dev(kB), nullptr, 32768, 1, 32, 128, 8, 0, 0.0f), LTXA_E_NULL);
+  EXPECT(pack(0, 1, 32, 128, 8, 0, 0.0f), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 0, 32, 128, 8, 0, 0.0f), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 1, 32, 130, 8, 0, 0.0f), LTXA_E_ALIGN);
+  EXPECT(pack(32768, 1, 32, 258, 8, 0, 0.0f), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 1, 32, 128, 8, 2, 0.0f), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, -2.0f), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, std::numeric_limits<float>::quiet_NaN()), LTXA_E_SHAPE);
+  EXPECT(pack(32768, 1, 32, 40, 8, 1, 0.0f), LTXA_E_ALIGN);  // split: head_dim % 16
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f, kA + 8), LTXA_E_ALIGN);
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f, kA, kB, kD + 8), LTXA_E_ALIGN);
+  EXPECT(pack(32768, 1, 30, 128, 8, 0, 0.0f), LTXA_E_DIVISIBILITY);
+  EXPECT(pack(32761, 1, 32, 128, 8, 0, 0.0f), LTXA_E_DIVISIBILITY);
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f, kA, kA + 4096), LTXA_E_ALIAS);
+  EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f, kA, kB, kB + 4096), LTXA_E_ALIAS);
+  EXPECT(pack(int64_t(1) << 40, int64_t(1) << 13, 32, 128, 8, 0, 0.0f), LTXA_E_RANGE);
+  EXPECT(pack(int64_t(1) << 36, 1, 8, 128, 8, 0, 0.0f), LTXA_E_RANGE);  // grid above 2^31 workgroups
+}
+
 void mul_checks() {
   EXPECT(int(ltxa::mul_capped(INT64_MAX, INT64_MAX)), -1);
   EXPECT(int(ltxa::mul_capped(-1, 5)), -1);
@@ -236,6 +296,7 @@ int main() {
   attn_checks();
   pack_rope_checks();
   rope_opts_checks();
+  rope_table_checks();
   mul_checks();
   std::printf("validate_check: %d cases, %d failures\n", g_cases, g_failures);
   return g_failures == 0 ? 0 : 1;

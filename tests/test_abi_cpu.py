@@ -253,6 +253,52 @@ def test_pack_rope_ex_errors(L):
     assert f(A, B, C, 232, 3, mp3, 1, 4, 40, 2, 1e4, _opts(rope_type="split"), None) == ltxa.LTXA_E_ALIGN
 
 
+def test_rope_table_errors(L):
+    f = L.ltxa_rope_table
+    mp3 = _mp(3, 7, 11)
+    # pos, n, axes, max_pos, head_dim, theta, opts, table, stream
+    assert f(None, 232, 3, mp3, 64, 1e4, None, B, None) == ltxa.LTXA_E_NULL
+    assert f(C, 232, 3, None, 64, 1e4, None, B, None) == ltxa.LTXA_E_NULL
+    assert f(C, 232, 3, mp3, 64, 1e4, None, None, None) == ltxa.LTXA_E_NULL
+    assert f(C, 0, 3, mp3, 64, 1e4, None, B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 4, mp3, 64, 1e4, None, B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 3, mp3, 63, 1e4, None, B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 3, mp3, 64, -1.0, None, B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 3, mp3, 62, 1e4, None, B, None) == ltxa.LTXA_E_ALIGN
+    assert f(C, 232, 3, mp3, 64, 1e4, None, B + 4, None) == ltxa.LTXA_E_ALIGN
+    # The table serves the head-shared grid and holds unscaled angles.
+    assert f(C, 232, 3, mp3, 64, 1e4, _opts(grid_heads=4), B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 3, mp3, 64, 1e4, _opts(out_scale=0.5), B, None) == ltxa.LTXA_E_SHAPE
+    assert f(C, 232, 3, mp3, 64, 1e4, _raw_opts(2, 0, 0, 0, 0, 0), B, None) == ltxa.LTXA_E_SHAPE
+    # 232 tokens x 3 axes of int32 positions start 16 bytes below the table.
+    assert f(B - 16, 232, 3, mp3, 64, 1e4, None, B, None) == ltxa.LTXA_E_ALIAS
+    assert f(C, 1 << 38, 3, mp3, 64, 1e4, None, B, None) == ltxa.LTXA_E_RANGE
+
+
+def test_pack_rope_table_errors(L):
+    f = L.ltxa_sp_pack_rope_table
+    # src, dst, table, n, batch, heads, head_dim, world_size, rope_type, out_scale, stream
+    good = (232, 1, 4, 64, 2, 0, 0.0)
+    assert f(None, B, C, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, None, C, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, None, *good, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, 0, 1, 4, 64, 2, 0, 0.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 1, 4, 63, 2, 0, 0.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 1, 4, 64, 0, 0, 0.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, 232, 1, 4, 64, 2, 2, 0.0, None) == ltxa.LTXA_E_SHAPE
+    for sc in (-1.0, float("inf"), float("nan")):
+        assert f(A, B, C, 232, 1, 4, 64, 2, 0, sc, None) == ltxa.LTXA_E_SHAPE, sc
+    assert f(A, B, C, 232, 1, 4, 62, 2, 0, 0.0, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, 232, 1, 4, 40, 2, 1, 0.0, None) == ltxa.LTXA_E_ALIGN  # SPLIT: head_dim % 16
+    assert f(A + 8, B, C, *good, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C + 8, *good, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, C, 232, 1, 4, 64, 3, 0, 0.0, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, C, 231, 1, 4, 64, 2, 0, 0.0, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, A + 256, C, *good, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, B + 256, *good, None) == ltxa.LTXA_E_ALIAS
+    assert f(A, B, C, 1 << 40, 1 << 13, 4, 64, 2, 0, 0.0, None) == ltxa.LTXA_E_RANGE
+
+
 def test_sp_share_bookkeeping():
     s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096

@@ -248,3 +248,53 @@ def test_rope_ex_out_scale():
     ok, exact = rope_ok(f64(scaled), ref, c * x64)
     assert ok.all(), f"{np.count_nonzero(~ok)} outputs off"
     assert exact > 0.995
+
+
+# (rope_type, fp64 angles, cell middles, log2-domain output scale)
+TABLE_VARIANTS = [("interleaved", False, False, False), ("interleaved", False, False, True),
+                  ("split", True, True, False), ("split", False, False, True),
+                  ("interleaved", True, False, True), ("interleaved", False, True, False)]
+
+
+@pytest.mark.parametrize("name,heads,P,which", PACK_ROPE_CASES)
+def test_pack_rope_table_equals_pack_rope(name, heads, P, which):
+    w = wl.WORKLOADS[name]
+    print(f"pack_rope_table {name} H={heads} P={P} {which}", flush=True)
+    q, k, _ = wl.qkv(w, heads=heads)
+    qpos, kpos = wl.positions(w)
+    x, pos, max_pos = (q, qpos, w.q_max_pos) if which == "q" else (k, kpos, w.k_max_pos)
+    xg, pg = x.to(DEV), torch.from_numpy(pos).to(DEV)
+    D = x.shape[3]
+    for rope_type, fp64_angles, middle, scaled in TABLE_VARIANTS:
+        if rope_type == "split" and D % 16:
+            continue
+        c = ltxa.log2_domain_scale(w.scale) if scaled else 0.0
+        topts = ltxa.rope_opts(fp64_angles=fp64_angles, middle=middle)
+        table = ltxa.rope_table(pg, max_pos, D, w.theta, opts=topts)
+        got = ltxa.sp_pack_rope_table(xg, table, P, rope_type=rope_type, out_scale=c)
+        opts = ltxa.rope_opts(rope_type=rope_type, fp64_angles=fp64_angles, middle=middle, out_scale=c)
+        want = ltxa.sp_pack_rope(xg, pg, max_pos, P, w.theta, opts=opts)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(got), bits(want)), (rope_type, fp64_angles, middle, scaled)
+
+
+@pytest.mark.parametrize("name,which", [("share_32768", "q"), ("tiny_231", "q"), ("cross_24576x1000", "k"),
+                                        ("ragged_32761", "q")])
+@pytest.mark.parametrize("fp64_angles,middle", [(False, False), (True, False), (False, True)])
+def test_rope_table_matches_oracle_angles(name, which, fp64_angles, middle):
+    # Pins the table to the oracle's angle schedule (not to another kernel):
+    # fp32 angles are within a few fp32 ulps of (cos, sin) of the exact
+    # angle; fp64 angles are the exact values rounded to fp32.
+    w = wl.WORKLOADS[name]
+    print(f"rope_table {name} {which} fp64={fp64_angles} middle={middle}", flush=True)
+    qpos, kpos = wl.positions(w)
+    pos, max_pos = (qpos, w.q_max_pos) if which == "q" else (kpos, w.k_max_pos)
+    D = w.head_dim
+    table = ltxa.rope_table(torch.from_numpy(pos).to(DEV), max_pos, D, w.theta,
+                            opts=ltxa.rope_opts(fp64_angles=fp64_angles, middle=middle))
+    torch.cuda.synchronize()
+    phi = oracle.rope_angles(pos, max_pos, D, w.theta, middle=middle)
+    want = np.stack([np.cos(phi), np.sin(phi)], axis=-1)
+    err = np.max(np.abs(f64(table) - want))
+    tol = 2.0 ** -23 if fp64_angles else 2.0 ** -20
+    assert err <= tol, f"max |table - (cos, sin)| = {err:.3e}"

@@ -48,6 +48,19 @@ hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* s
                            int32_t head_dim, int32_t ranks, const RopeMode& mode, const RopeTable& table,
                            const RopeInner& inner, hipStream_t stream);
 
+// Angle table of the head-shared grid: table_out[n][i] = (cos, sin) of pair i
+// of token n, fp32, head_dim/2 pairs per token (mode.f64 and mode.mid as for
+// launch_rope_any; the split, inner and out_scale fields are not used).
+hipError_t launch_rope_angles(const int32_t* pos, float* table_out, int64_t n_tokens, int32_t axes,
+                              int32_t head_dim, const RopeMode& mode, const RopeTable& table,
+                              hipStream_t stream);
+
+// launch_rope_any's pack (ranks head shards) with the angles taken from such a
+// table, each (cos, sin) multiplied by out_scale.
+hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const float* table, int64_t n_tokens,
+                                  int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, bool split,
+                                  float out_scale, hipStream_t stream);
+
 // Attention over [batch, nq, heads, head_dim] operands.  The output row of
 // (batch entry bb, token n, head h) is written at head slot
 // (bb / out_batch) * heads + h of token n of output batch entry

@@ -178,6 +178,28 @@ LTXA_EXPORT int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* 
                      stream);
 }
 
+LTXA_EXPORT int ltxa_rope_table(const int32_t* pos, int64_t n_tokens, int32_t axes, const double* max_pos,
+                                int32_t head_dim, double theta, const ltxa_rope_opts* opts, float* table,
+                                void* stream) {
+  const int rc = ltxa::check_rope_angles(pos, n_tokens, axes, max_pos, head_dim, theta, opts, table);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_rope_angles(pos, table, n_tokens, axes, head_dim, rope_mode(opts),
+                                                rope_table(head_dim, axes, max_pos, theta),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_sp_pack_rope_table(const void* src, void* dst, const float* table, int64_t n_tokens,
+                                        int64_t batch, int32_t heads, int32_t head_dim, int32_t world_size,
+                                        int32_t rope_type, float out_scale, void* stream) {
+  const int rc = ltxa::check_pack_rope_table(src, dst, table, n_tokens, batch, heads, head_dim, world_size,
+                                             rope_type, out_scale);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_rope_pack_table(
+      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), table, n_tokens, batch, heads, head_dim,
+      world_size, rope_type == LTXA_ROPE_SPLIT, out_scale != 0.0f ? out_scale : 1.0f,
+      static_cast<hipStream_t>(stream)));
+}
+
 LTXA_EXPORT int ltxa_attn_fwd_log2q(const void* q, const void* k, const void* v, void* o, float* lse,
                                     int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk_pad,
                                     int64_t nk_valid, void* stream) {

@@ -266,6 +266,140 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
   }
 }
 
+// Angle table of the shared grid (the pages' precomputed frequencies,
+// precompute_ltx_freqs_cis, applied later by apply_ltx_rotary_emb): entry
+// (n, i) = (cos, sin) of pair i of token n, from the same turn() as the
+// kernels above, unscaled, so a rotation read from the table equals the one
+// computed in place bit for bit.  One thread per (token, pair).
+template <bool F64>
+__global__ __launch_bounds__(kThreads) void rope_angles_kernel(const int32_t* __restrict__ pos,
+                                                               float2* __restrict__ out, int64_t n_tokens,
+                                                               int32_t axes, int32_t half, int32_t log2_half,
+                                                               double mid, RopeTable table) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= n_tokens * half) return;
+  // A shift when half is a power of two (log2_half >= 0): 64-bit divides are
+  // software loops.
+  const int64_t n = log2_half >= 0 ? t >> log2_half : t / half;
+  const int i = static_cast<int>(t - n * half);
+  const int a = table.axis[i];
+  float c = 1.0f, s = 0.0f;
+  if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[i], c, s);
+  out[t] = float2{c, s};
+}
+
+// Pack + rotary with the angles read from that table.  Layout of the plain
+// pack rather than of the shared-grid kernel: one thread owns one pair group
+// (16 bytes of each head row; split pairing: 16 bytes in each half) of one
+// token row and rank, and rotates that rank's heads/ranks rows of it, so a
+// wave reads and writes whole 16-byte columns of consecutive token rows.
+// Workgroups are dealt so that the ranks of the same token rows are
+// consecutive logical workgroups on one XCD, which then reads each table row
+// into its L2 once (dealt round-robin, every XCD's L2 fetches the whole
+// table: +9 % in a timing probe).  Measured on MI355X on the [1, 32768, 32,
+// 128] -> 8 ranks tensor: 91.5-92.3 us, against 93.8-94.6 us for the
+// shared-grid kernel, which computes its sin/cos itself; building the table
+// takes ~10 us more, so the table pays where it serves several tensors or
+// layers, as the pages' precomputed frequencies do.
+template <bool SPLIT>
+__global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* __restrict__ src,
+                                                                   u32x4* __restrict__ dst,
+                                                                   const float4* __restrict__ tab,
+                                                                   int64_t n_tokens, int64_t batch,
+                                                                   int32_t heads, int32_t head_dim,
+                                                                   int32_t ranks, int32_t nblocks,
+                                                                   int32_t log2_ranks, int32_t log2_groups,
+                                                                   float out_scale) {
+  constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
+  const int groups = head_dim / (2 * PPT);
+  const int half = head_dim / 2;
+  const int row = head_dim / 8;  // 16-byte vectors per head row
+  // Index arithmetic is a large part of a thread's work here: shifts when
+  // the rank and group counts are powers of two (log2 >= 0), and no divide
+  // by n_tokens for one batch entry.  (64-bit divides are software loops.)
+  const uint32_t lid = static_cast<uint32_t>(xcd_contiguous(blockIdx.x, nblocks));
+  uint32_t p, blk;
+  if (log2_ranks >= 0) {
+    p = lid & ((1u << log2_ranks) - 1);
+    blk = lid >> log2_ranks;
+  } else {
+    p = lid % static_cast<uint32_t>(ranks);
+    blk = lid / static_cast<uint32_t>(ranks);
+  }
+  const int64_t t = static_cast<int64_t>(blk) * kThreads + threadIdx.x;
+  int64_t r;  // token row b * n_tokens + n
+  int g;
+  if (log2_groups >= 0) {
+    r = t >> log2_groups;
+    g = static_cast<int>(t & (groups - 1));
+  } else {
+    r = t / groups;
+    g = static_cast<int>(t - r * groups);
+  }
+  if (r >= batch * n_tokens) return;
+  int64_t b = 0, n = r;
+  if (batch > 1) {
+    b = r / n_tokens;
+    n = r - b * n_tokens;
+  }
+
+  float c[PPT], s[PPT];
+  const float4* e = tab + (n * half + PPT * g) / 2;  // pairs PPT g .. PPT g + PPT - 1, two per float4
+#pragma unroll
+  for (int k = 0; k < PPT / 2; ++k) {
+    const float4 v = e[k];
+    c[2 * k] = v.x * out_scale;
+    s[2 * k] = v.y * out_scale;
+    c[2 * k + 1] = v.z * out_scale;
+    s[2 * k + 1] = v.w * out_scale;
+  }
+
+  // Vector g (and, split, g + row / 2) of this rank's head rows: the rows
+  // are consecutive in both layouts, `row` vectors apart.
+  const int32_t hl = heads / ranks;
+  const u32x4* from = src + (r * heads + int64_t(p) * hl) * row + g;
+  u32x4* to = dst + ((int64_t(p) * batch + b) * n_tokens + n) * hl * row + g;
+  auto rotate = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPLIT) {
+      u32x4 lo = __builtin_nontemporal_load(from + j * row);
+      u32x4 hi = __builtin_nontemporal_load(from + j * row + row / 2);
+      rotate_split(lo, hi, c, s);
+      __builtin_nontemporal_store(lo, to + j * row);
+      __builtin_nontemporal_store(hi, to + j * row + row / 2);
+    } else {
+      __builtin_nontemporal_store(rotate_interleaved(__builtin_nontemporal_load(from + j * row), c, s),
+                                  to + j * row);
+    }
+  };
+  // Whole groups of kRowsInFlight rows: all loads issued before the first
+  // rotation (the compiler keeps that order: the pointers are restrict).
+  int32_t j0 = 0;
+  for (; j0 + kRowsInFlight <= hl; j0 += kRowsInFlight) {
+    if constexpr (SPLIT) {
+      u32x4 lo[kRowsInFlight], hi[kRowsInFlight];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        lo[u] = __builtin_nontemporal_load(from + (j0 + u) * row);
+        hi[u] = __builtin_nontemporal_load(from + (j0 + u) * row + row / 2);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        rotate_split(lo[u], hi[u], c, s);
+        __builtin_nontemporal_store(lo[u], to + (j0 + u) * row);
+        __builtin_nontemporal_store(hi[u], to + (j0 + u) * row + row / 2);
+      }
+    } else {
+      u32x4 w[kRowsInFlight];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) w[u] = __builtin_nontemporal_load(from + (j0 + u) * row);
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u)
+        __builtin_nontemporal_store(rotate_interleaved(w[u], c, s), to + (j0 + u) * row);
+    }
+  }
+  for (; j0 < hl; ++j0) rotate(j0);
+}
+
 template <bool SPLIT, bool F64>
 hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
                        const int32_t* pos, int64_t n_tokens, int32_t axes, int64_t batch, int32_t heads,
@@ -320,6 +454,52 @@ hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* s
                                              ranks, mode, table, inner, stream)
                   : launch_mode<false, false>(src, dst, src2, dst2, pos, n_tokens, axes, batch, heads, head_dim,
                                               ranks, mode, table, inner, stream);
+}
+
+
+hipError_t launch_rope_angles(const int32_t* pos, float* table_out, int64_t n_tokens, int32_t axes,
+                              int32_t head_dim, const RopeMode& mode, const RopeTable& table,
+                              hipStream_t stream) {
+  (void)hipGetLastError();  // report only this launch's error
+  const int32_t half = head_dim / 2;
+  const int64_t blocks = (n_tokens * half + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  float2* out = reinterpret_cast<float2*>(table_out);
+  const int32_t log2_half = (half & (half - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(half)) : -1;
+  if (mode.f64)
+    hipLaunchKernelGGL((rope_angles_kernel<true>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream,
+                       pos, out, n_tokens, axes, half, log2_half, mode.mid, table);
+  else
+    hipLaunchKernelGGL((rope_angles_kernel<false>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream,
+                       pos, out, n_tokens, axes, half, log2_half, mode.mid, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const float* table, int64_t n_tokens,
+                                  int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, bool split,
+                                  float out_scale, hipStream_t stream) {
+  (void)hipGetLastError();  // report only this launch's error
+  const int groups = head_dim / (split ? 16 : 8);
+  const int64_t per_rank = (batch * n_tokens * groups + kThreads - 1) / kThreads;
+  auto log2_or_minus1 = [](int32_t v) {
+    int k = 0;
+    while ((1 << k) < v) ++k;
+    return (1 << k) == v ? k : -1;
+  };
+  const int32_t lr = log2_or_minus1(ranks), lg = log2_or_minus1(groups);
+  const int64_t blocks = per_rank * ranks;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const float4* tab = reinterpret_cast<const float4*>(table);
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (split)
+    hipLaunchKernelGGL((rope_pack_table_kernel<true>), grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens,
+                       batch, heads, head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale);
+  else
+    hipLaunchKernelGGL((rope_pack_table_kernel<false>), grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens,
+                       batch, heads, head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale);
+  return hipGetLastError();
 }
 
 }  // namespace ltxa

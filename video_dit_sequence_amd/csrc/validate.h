@@ -194,6 +194,57 @@ inline int check_rope_opts(const ltxa_rope_opts* opts, int32_t heads, int32_t he
   return LTXA_OK;
 }
 
+// Angle table of the shared grid: table fp32 [n_tokens, head_dim/2, 2].
+// opts may be NULL; the table holds the unscaled angles of the head-shared
+// grid, so opts->grid_heads and opts->out_scale must be 0 (rope_type does not
+// change a pair's angle and is only checked for validity).
+inline int check_rope_angles(const int32_t* pos, int64_t n_tokens, int32_t axes, const double* max_pos,
+                             int32_t head_dim, double theta, const ltxa_rope_opts* opts, const float* table) {
+  if (!table) return LTXA_E_NULL;
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2 != 0) return LTXA_E_SHAPE;
+  if (!(std::isfinite(theta) && theta > 0.0)) return LTXA_E_SHAPE;
+  if ((head_dim * 2) % 16 != 0) return LTXA_E_ALIGN;
+  int rc = check_rope_tensor(table, pos, n_tokens, axes, max_pos, head_dim);
+  if (rc) return rc;
+  rc = check_rope_opts(opts, 1, head_dim, axes);
+  if (rc) return rc;
+  if (opts && (opts->grid_heads != 0 || opts->out_scale != 0.0f)) return LTXA_E_SHAPE;
+  const int64_t bytes = mul_capped(n_tokens, int64_t(head_dim) * 4);
+  if (bytes < 0 || mul_capped(n_tokens, axes) < 0) return LTXA_E_RANGE;
+  // Grid: one thread per (token, pair), 256 per workgroup, below 2^31 workgroups.
+  if (n_tokens * (head_dim / 2) >= (INT64_C(1) << 39)) return LTXA_E_RANGE;
+  if (overlap(table, bytes, pos, mul_capped(n_tokens, axes) * 4)) return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
+// Pack + rotary from an angle table: src [batch, n_tokens, heads, head_dim]
+// bf16 -> dst [world_size, batch, n_tokens, heads/world_size, head_dim] bf16,
+// table fp32 [n_tokens, head_dim/2, 2].  out_scale 0 means 1.
+inline int check_pack_rope_table(const void* src, const void* dst, const float* table, int64_t n_tokens,
+                                 int64_t batch, int32_t heads, int32_t head_dim, int32_t world_size,
+                                 int32_t rope_type, float out_scale) {
+  if (!src || !dst || !table) return LTXA_E_NULL;
+  if (n_tokens < 1 || batch < 1 || heads < 1 || world_size < 1) return LTXA_E_SHAPE;
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2 != 0) return LTXA_E_SHAPE;
+  if (!(rope_type == LTXA_ROPE_INTERLEAVED || rope_type == LTXA_ROPE_SPLIT)) return LTXA_E_SHAPE;
+  if (out_scale != 0.0f && check_out_scale(out_scale) != LTXA_OK) return LTXA_E_SHAPE;
+  if ((head_dim * 2) % 16 != 0) return LTXA_E_ALIGN;
+  if (rope_type == LTXA_ROPE_SPLIT && head_dim % 16 != 0) return LTXA_E_ALIGN;
+  if (!aligned16(src) || !aligned16(dst) || !aligned16(table)) return LTXA_E_ALIGN;
+  if (heads % world_size != 0 || n_tokens % world_size != 0) return LTXA_E_DIVISIBILITY;
+  const int64_t bytes = mul4_capped(batch, n_tokens, heads, int64_t(head_dim) * 2);
+  const int64_t tbytes = mul_capped(n_tokens, int64_t(head_dim) * 4);
+  if (bytes < 0 || tbytes < 0) return LTXA_E_RANGE;
+  // Grid: world_size * ceil(batch * n_tokens * groups / 256) workgroups below 2^31.
+  const int64_t groups = head_dim / (rope_type == LTXA_ROPE_SPLIT ? 16 : 8);
+  const int64_t threads = mul_capped(mul_capped(batch, n_tokens), groups);
+  if (threads < 0 || mul_capped((threads + 255) / 256, world_size) < 0 ||
+      (threads + 255) / 256 * world_size >= (INT64_C(1) << 31))
+    return LTXA_E_RANGE;
+  if (overlap(src, bytes, dst, bytes) || overlap(dst, bytes, table, tbytes)) return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
 // One tensor rotated in place: x [batch, n_tokens, heads, head_dim] bf16.
 inline int check_rope_ex(const void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
                          const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, double theta,

@@ -37,7 +37,7 @@ LTXA_E_RANGE = -7
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
            "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
            "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_attn_fwd_log2q",
-           "ltxa_attn_fwd_unpack_log2q")
+           "ltxa_attn_fwd_unpack_log2q", "ltxa_rope_table", "ltxa_sp_pack_rope_table")
 
 LTXA_ROPE_INTERLEAVED = 0
 LTXA_ROPE_SPLIT = 1
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.ltxa_attn_fwd_unpack_log2q.restype = ctypes.c_int
         L.ltxa_attn_fwd_unpack_log2q.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, i64,
                                                  i32, vp]
+        L.ltxa_rope_table.restype = ctypes.c_int
+        L.ltxa_rope_table.argtypes = [vp, i64, i32, dp, i32, ctypes.c_double, op, vp, vp]
+        L.ltxa_sp_pack_rope_table.restype = ctypes.c_int
+        L.ltxa_sp_pack_rope_table.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, vp]
         _lib = L
     return _lib
 
@@ -317,6 +321,61 @@ def sp_pack_rope(src: torch.Tensor, pos: torch.Tensor, max_pos, world_size: int,
         _check("ltxa_sp_pack_rope_ex", lib().ltxa_sp_pack_rope_ex(
             src.data_ptr(), out.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos),
             B, H, D, P, float(theta), ctypes.byref(opts), _stream_ptr(src)))
+    return out
+
+
+def rope_table(pos: torch.Tensor, max_pos, head_dim: int, theta: float = 10000.0,
+               opts: Optional[RopeOpts] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cos and sin of every (token, pair) of the head-shared grid
+    (``ltxa_rope_table``): float32 ``[N, head_dim/2, 2]``.
+
+    ``pos`` is an int32 ``[N, A]`` GPU tensor.  Of ``opts`` only ``fp64_angles``
+    and ``middle`` act; ``grid_heads`` and ``out_scale`` must be 0.  Rotating
+    with the table (:func:`sp_pack_rope_table`) equals rotating with the
+    positions, bit for bit.
+    """
+    _gpu(pos, "pos", torch.int32)
+    if pos.dim() != 2 or pos.shape[1] != len(max_pos):
+        raise ValueError("pos must be [N, A] with one max_pos per axis")
+    N = pos.shape[0]
+    if out is None:
+        out = torch.empty((N, max(int(head_dim) // 2, 1), 2), dtype=torch.float32, device=pos.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != N * (int(head_dim) // 2) * 2:
+        raise ValueError("out must hold N * head_dim/2 * 2 floats")
+    _check("ltxa_rope_table", lib().ltxa_rope_table(
+        pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos), int(head_dim), float(theta),
+        ctypes.byref(opts) if opts is not None else None, out.data_ptr(), _stream_ptr(pos)))
+    return out
+
+
+def sp_pack_rope_table(src: torch.Tensor, table: torch.Tensor, world_size: int, rope_type: str = "interleaved",
+                       out_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 ``[B, N, H, D]`` -> rotated ``[P, B, N, H/P, D]`` with the angles of
+    a :func:`rope_table` (``ltxa_sp_pack_rope_table``).
+
+    Equal, bit for bit, to :func:`sp_pack_rope` with the positions and options
+    the table was made from, this ``rope_type`` and ``out_scale``.
+    """
+    _gpu(src, "src", torch.bfloat16)
+    _gpu(table, "table", torch.float32)
+    B, N, H, D = src.shape
+    P = int(world_size)
+    types = {"interleaved": LTXA_ROPE_INTERLEAVED, "split": LTXA_ROPE_SPLIT}
+    if rope_type not in types:
+        raise ValueError("rope_type must be 'interleaved' or 'split'")
+    if table.numel() != N * (D // 2) * 2:
+        raise ValueError("table must be [N, D/2, 2]")
+    if out is None:
+        if P < 1 or H % P:
+            _check("ltxa_sp_pack_rope_table", LTXA_E_DIVISIBILITY if P >= 1 else LTXA_E_SHAPE)
+        out = torch.empty((P, B, N, H // P, D), dtype=src.dtype, device=src.device)
+    _gpu(out, "out", torch.bfloat16)
+    if out.numel() != src.numel():
+        raise ValueError("out has the wrong number of elements")
+    _check("ltxa_sp_pack_rope_table", lib().ltxa_sp_pack_rope_table(
+        src.data_ptr(), out.data_ptr(), table.data_ptr(), N, B, H, D, P, types[rope_type], float(out_scale),
+        _stream_ptr(src)))
     return out
 
 
