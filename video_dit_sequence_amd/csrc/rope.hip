@@ -297,11 +297,11 @@ __global__ __launch_bounds__(kThreads) void rope_angles_kernel(const int32_t* __
 // consecutive logical workgroups on one XCD, which then reads each table row
 // into its L2 once (dealt round-robin, every XCD's L2 fetches the whole
 // table: +9 % in a timing probe).  Measured on MI355X on the [1, 32768, 32,
-// 128] -> 8 ranks tensor: 91.5-92.3 us, against 93.8-94.6 us for the
+// 128] -> 8 ranks tensor: 90.4-91.0 us, against 93.9-94.6 us for the
 // shared-grid kernel, which computes its sin/cos itself; building the table
 // takes ~10 us more, so the table pays where it serves several tensors or
 // layers, as the pages' precomputed frequencies do.
-template <bool SPLIT>
+template <bool SPLIT, int ROW, bool WHOLE>
 __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* __restrict__ src,
                                                                    u32x4* __restrict__ dst,
                                                                    const float4* __restrict__ tab,
@@ -311,9 +311,12 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
                                                                    int32_t log2_ranks, int32_t log2_groups,
                                                                    float out_scale) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
-  const int groups = head_dim / (2 * PPT);
-  const int half = head_dim / 2;
-  const int row = head_dim / 8;  // 16-byte vectors per head row
+  // ROW > 0 fixes the 16-byte vectors per head row (head_dim / 8) at compile
+  // time, so that the index arithmetic folds into shifts and constants;
+  // WHOLE: heads / ranks is a multiple of kRowsInFlight (no partial group).
+  const int row = ROW > 0 ? ROW : head_dim / 8;
+  const int groups = SPLIT ? row / 2 : row;
+  const int half = row * 4;
   // Index arithmetic is a large part of a thread's work here: shifts when
   // the rank and group counts are powers of two (log2 >= 0), and no divide
   // by n_tokens for one batch entry.  (64-bit divides are software loops.)
@@ -397,7 +400,8 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
         __builtin_nontemporal_store(rotate_interleaved(w[u], c, s), to + (j0 + u) * row);
     }
   }
-  for (; j0 < hl; ++j0) rotate(j0);
+  if constexpr (!WHOLE)
+    for (; j0 < hl; ++j0) rotate(j0);
 }
 
 template <bool SPLIT, bool F64>
@@ -493,12 +497,22 @@ hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const floa
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
   const dim3 grid(static_cast<uint32_t>(blocks));
-  if (split)
-    hipLaunchKernelGGL((rope_pack_table_kernel<true>), grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens,
-                       batch, heads, head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale);
-  else
-    hipLaunchKernelGGL((rope_pack_table_kernel<false>), grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens,
-                       batch, heads, head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens, batch, heads, head_dim, ranks,
+                       static_cast<int32_t>(blocks), lr, lg, out_scale);
+  };
+  // Specialised for the common shapes: head_dim 128 or 64 with whole groups
+  // of kRowsInFlight heads per rank; every other shape takes the general form.
+  const bool whole = (heads / ranks) % kRowsInFlight == 0;
+  if (split) {
+    if (whole && head_dim == 128) go(rope_pack_table_kernel<true, 16, true>);
+    else if (whole && head_dim == 64) go(rope_pack_table_kernel<true, 8, true>);
+    else go(rope_pack_table_kernel<true, 0, false>);
+  } else {
+    if (whole && head_dim == 128) go(rope_pack_table_kernel<false, 16, true>);
+    else if (whole && head_dim == 64) go(rope_pack_table_kernel<false, 8, true>);
+    else go(rope_pack_table_kernel<false, 0, false>);
+  }
   return hipGetLastError();
 }
 
