@@ -7,11 +7,12 @@ every rank's 4 heads, and unpack the output.  Every part is exactly 8x one
 rank's share, so the rate equals one rank's.  Inputs are seeded synthetic
 bf16 N(0,1) tensors already resident in HBM.
 
-The default path takes four launches (``--path fused``): Q and K are packed
-and rotated in one pass each (the Q pass also multiplies by
-scale * log2(e) before its one rounding), V is packed, and the attention
-kernel takes those log2-domain queries as given and writes its output in
-token order.  ``--path unfused`` times the six-launch sequence (pack x3,
+The default path takes four launches (``--path fused``): the (cos, sin)
+table of the tokens' positions is built (in a model, once per forward pass
+for every layer; here once per step), Q and K are packed and rotated with it
+in one launch (the Q half also multiplies by scale * log2(e) before its one
+rounding), V is packed, and the attention kernel takes those log2-domain
+queries as given and writes its output in token order.  ``--path unfused`` times the six-launch sequence (pack x3,
 rotary, attention, unpack), in which the attention kernel scales and
 rounds Q itself.
 
@@ -244,6 +245,7 @@ def main():
         sys.exit(2)
 
     global torch
+    import numpy as np
     import torch
     from video_dit_sequence_amd import ltxa
     from video_dit_sequence_amd import workloads as wl
@@ -270,13 +272,18 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     if args.path == "fused":
-        phase_names = ("pack_rope_qk", "pack_v", "attn_fwd")
+        phase_names = ("rope_table", "pack_rope_qk", "pack_v", "attn_fwd")
 
         c = ltxa.log2_domain_scale(w.scale)
+        # Self-attention: Q and K turn by the same angles.  The step builds
+        # their table (in a model, once per forward pass for every layer)
+        # and then exchanges and rotates Q and K in one launch.
+        assert np.array_equal(qpos, kpos) and list(w.q_max_pos) == list(w.k_max_pos)
+        table = share.rope_table_buffer(dev)
 
         def launches():
-            ltxa.sp_pack_rope(q, pos, w.q_max_pos, P, w.theta, out=qs, out_scale=c)
-            yield ltxa.sp_pack_rope(k, pos, w.k_max_pos, P, w.theta, out=ks)
+            yield ltxa.rope_table(pos, w.q_max_pos, D, w.theta, out=table)
+            yield ltxa.sp_pack_rope_qk_table(q, k, table, P, q_scale=c, q_out=qs, k_out=ks)
             yield ltxa.sp_pack(v, P, out=vs)
             yield ltxa.attn_fwd_unpack(qs, ks, vs, nk_valid=w.nk_valid, out=out, q_log2=True)
     else:
@@ -329,8 +336,10 @@ def main():
     attn_tflops = attn_flop / (avg["attn_fwd"] * 1e-3) / 1e12
     traffic = traffic_per_launch()
     tensor_bytes = 2.0 * B * N * H * D                  # one bf16 [B, N, H, D] tensor
+    table_bytes = 4.0 * N * D                           # fp32 (cos, sin) per token and pair
     phase_bytes = {                                     # algorithmic HBM bytes (read + write)
-        "pack_rope_qk": 2 * 2 * tensor_bytes + 2 * N * 3 * 4,
+        "rope_table": N * 3 * 4 + table_bytes,
+        "pack_rope_qk": 2 * 2 * tensor_bytes + table_bytes,
         "pack_v": 2 * tensor_bytes,
         "pack_qkv": 3 * 2 * tensor_bytes,
         "rope_qk": 2 * 2 * tensor_bytes + 2 * N * 3 * 4,

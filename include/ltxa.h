@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 105 /* major*100 + minor */
+#define LTXA_VERSION 106 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -324,6 +324,27 @@ int ltxa_rope_table(const int32_t* pos, int64_t n_tokens, int32_t axes, const do
 int ltxa_sp_pack_rope_table(const void* src, void* dst, const float* table, int64_t n_tokens,
                             int64_t batch, int32_t heads, int32_t head_dim, int32_t world_size,
                             int32_t rope_type, float out_scale, void* stream);
+
+/*
+ * ltxa_sp_pack_rope_qk_table -- ltxa_sp_pack_rope_table of Q and of K in one
+ * launch, for self-attention, where Q and K of a token turn by the same
+ * angles (the rotary embedding page's precomputed frequencies, applied to
+ * the queries and the keys alike).  Each table entry is read once for both.
+ *   q, k: bf16 [batch, n_tokens, heads, head_dim], read only (they may
+ *     overlap each other).
+ *   q_dst, k_dst: bf16 [world_size, batch, n_tokens, heads/world_size,
+ *     head_dim], written.
+ *   q_scale, k_scale: the out_scale of each (0 = none).
+ *   table, rope_type and the sizes: as in ltxa_sp_pack_rope_table.
+ * q_dst and k_dst equal, bit for bit, ltxa_sp_pack_rope_table(q, q_dst, ...,
+ * q_scale) and ltxa_sp_pack_rope_table(k, k_dst, ..., k_scale).
+ * Errors: those of ltxa_sp_pack_rope_table for either pair, and E_ALIAS when
+ * q_dst overlaps k or k_dst, or k_dst overlaps q.
+ */
+int ltxa_sp_pack_rope_qk_table(const void* q, void* q_dst, float q_scale, const void* k, void* k_dst,
+                               float k_scale, const float* table, int64_t n_tokens, int64_t batch,
+                               int32_t heads, int32_t head_dim, int32_t world_size, int32_t rope_type,
+                               void* stream);
 
 /*
  * Log2-domain queries.  The attention computes its softmax in base 2: with

@@ -276,6 +276,30 @@ void rope_table_checks() {
   EXPECT(pack(32768, 1, 32, 128, 8, 0, 0.0f, kA, kB, kB + 4096), LTXA_E_ALIAS);
   EXPECT(pack(int64_t(1) << 40, int64_t(1) << 13, 32, 128, 8, 0, 0.0f), LTXA_E_RANGE);
   EXPECT(pack(int64_t(1) << 36, 1, 8, 128, 8, 0, 0.0f), LTXA_E_RANGE);  // grid above 2^31 workgroups
+
+  // Q and K in one launch: each pair as above, and no destination on the
+  // other pair's tensors (256 MiB per tensor at these sizes).
+  auto qk = [&](uintptr_t q, uintptr_t qd, float qs, uintptr_t k, uintptr_t kd, float ks, int32_t type = 0,
+                int64_t n = 32768) {
+    return ltxa::check_pack_rope_qk_table(dev(q), dev(qd), qs, dev(k), dev(kd), ks, devf(kD), n, 1, 32, 128, 8,
+                                          type);
+  };
+  EXPECT(qk(kA, kB, 0.18033688f, kC, kE, 0.0f), LTXA_OK);
+  EXPECT(qk(kA, kB, 0.0f, kA, kE, 0.0f, 1), LTXA_OK);  // the sources may overlap
+  EXPECT(qk(kA, kB, 0.0f, 0, kE, 0.0f), LTXA_E_NULL);
+  EXPECT(qk(kA, kB, 0.0f, kC, 0, 0.0f), LTXA_E_NULL);
+  EXPECT(qk(kA, kB, 0.0f, kC, kE, -1.0f), LTXA_E_SHAPE);
+  EXPECT(qk(kA, kB, 0.0f, kC + 8, kE, 0.0f), LTXA_E_ALIGN);
+  EXPECT(qk(kA, kB, 0.0f, kC, kE, 0.0f, 0, 32761), LTXA_E_DIVISIBILITY);
+  EXPECT(qk(kA, kB, 0.0f, kB + 4096, kE, 0.0f), LTXA_E_ALIAS);  // q_dst on k
+  EXPECT(qk(kA, kB, 0.0f, kC, kB + 4096, 0.0f), LTXA_E_ALIAS);  // the destinations overlap
+  EXPECT(qk(kA, kB, 0.0f, kC, kA + 4096, 0.0f), LTXA_E_ALIAS);  // k_dst on q
+  EXPECT(qk(kA, kB, 0.0f, kC, kD + 4096, 0.0f), LTXA_E_ALIAS);  // k_dst on the table
+  // 2^31 tokens: a grid of 2^30 workgroups per tensor is valid for one
+  // tensor, not for two (16 TiB tensors, so the addresses are 32 TiB apart).
+  constexpr uintptr_t kT = uintptr_t(1) << 45;
+  EXPECT(pack(int64_t(1) << 31, 1, 32, 128, 8, 0, 0.0f, kT, 2 * kT), LTXA_OK);
+  EXPECT(qk(kT, 2 * kT, 0.0f, 3 * kT, 4 * kT, 0.0f, 0, int64_t(1) << 31), LTXA_E_RANGE);
 }
 
 void mul_checks() {

@@ -299,6 +299,23 @@ def test_pack_rope_table_errors(L):
     assert f(A, B, C, 1 << 40, 1 << 13, 4, 64, 2, 0, 0.0, None) == ltxa.LTXA_E_RANGE
 
 
+def test_pack_rope_qk_table_errors(L):
+    f = L.ltxa_sp_pack_rope_qk_table
+    # q, q_dst, q_scale, k, k_dst, k_scale, table, n, batch, heads, head_dim, world_size, rope_type, stream
+    sizes = (232, 1, 4, 64, 2, 0)
+    assert f(A, B, 0.0, None, E, 0.0, C, *sizes, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, 0.0, D_, None, 0.0, C, *sizes, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, 0.0, D_, E, 0.0, None, *sizes, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, 0.0, D_, E, -1.0, C, *sizes, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, float("nan"), D_, E, 0.0, C, *sizes, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, 0.0, D_ + 8, E, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, B, 0.0, D_, E, 0.0, C, 231, 1, 4, 64, 2, 0, None) == ltxa.LTXA_E_DIVISIBILITY
+    assert f(A, B, 0.0, B + 256, E, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIAS   # q_dst on k
+    assert f(A, B, 0.0, D_, B + 256, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIAS  # both destinations
+    assert f(A, B, 0.0, D_, A + 256, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIAS  # k_dst on q
+    assert f(A, B, 0.0, D_, C + 256, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIAS  # k_dst on the table
+
+
 def test_sp_share_bookkeeping():
     s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096

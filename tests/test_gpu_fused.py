@@ -256,6 +256,28 @@ TABLE_VARIANTS = [("interleaved", False, False, False), ("interleaved", False, F
                   ("interleaved", True, False, True), ("interleaved", False, True, False)]
 
 
+@pytest.mark.parametrize("prescale_q", [True, False])
+def test_self_attention_table_form_equals_per_tensor_form(prescale_q):
+    # sp_attention turns self-attention's Q and K with one angle table in one
+    # launch; a K position tensor of its own (equal values) takes the
+    # one-call-per-tensor form.  The results agree bit for bit, and so does
+    # a table the caller built once and passes in.
+    w = wl.WORKLOADS["ragged_32761"]
+    print(f"sp_attention table form ragged_32761 P=8 prescale={prescale_q}", flush=True)
+    q, k, v = (t.to(DEV) for t in wl.qkv(w))
+    qpos, _ = wl.positions(w)
+    pg = torch.from_numpy(qpos).to(DEV)
+    share = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
+    share.set_seqlen(w.nq_valid)
+    a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, prescale_q=prescale_q).clone()
+    table = ltxa.rope_table(pg, w.q_max_pos, 128, w.theta)
+    b = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, prescale_q=prescale_q, q_rope_table=table).clone()
+    c = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, k_pos=pg.clone(), prescale_q=prescale_q)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(c))
+    assert np.array_equal(bits(b), bits(c))
+
+
 @pytest.mark.parametrize("name,heads,P,which", PACK_ROPE_CASES)
 def test_pack_rope_table_equals_pack_rope(name, heads, P, which):
     w = wl.WORKLOADS[name]
@@ -276,6 +298,34 @@ def test_pack_rope_table_equals_pack_rope(name, heads, P, which):
         want = ltxa.sp_pack_rope(xg, pg, max_pos, P, w.theta, opts=opts)
         torch.cuda.synchronize()
         assert np.array_equal(bits(got), bits(want)), (rope_type, fp64_angles, middle, scaled)
+
+
+@pytest.mark.parametrize("name,heads,P,which", PACK_ROPE_CASES)
+def test_pack_rope_qk_table_equals_two_table_calls(name, heads, P, which):
+    # One launch for Q and K (self-attention: the same positions) equals the
+    # two one-tensor calls, each with its own scale.  The second tensor is
+    # the first with its heads reversed and negated; a third pass hands the
+    # same tensor in as both sources.
+    w = wl.WORKLOADS[name]
+    print(f"pack_rope_qk_table {name} H={heads} P={P} {which}", flush=True)
+    q, k, _ = wl.qkv(w, heads=heads)
+    qpos, kpos = wl.positions(w)
+    x, pos, max_pos = (q, qpos, w.q_max_pos) if which == "q" else (k, kpos, w.k_max_pos)
+    xg, pg = x.to(DEV), torch.from_numpy(pos).to(DEV)
+    x2 = (-xg.flip(2)).contiguous()
+    D = x.shape[3]
+    for rope_type, fp64_angles, middle, scaled in TABLE_VARIANTS:
+        if rope_type == "split" and D % 16:
+            continue
+        c = ltxa.log2_domain_scale(w.scale) if scaled else 0.0
+        table = ltxa.rope_table(pg, max_pos, D, w.theta, opts=ltxa.rope_opts(fp64_angles=fp64_angles, middle=middle))
+        for second, c2 in ((x2, 0.0), (x2, 0.5), (xg, c)):
+            got_q, got_k = ltxa.sp_pack_rope_qk_table(xg, second, table, P, rope_type=rope_type, q_scale=c, k_scale=c2)
+            want_q = ltxa.sp_pack_rope_table(xg, table, P, rope_type=rope_type, out_scale=c)
+            want_k = ltxa.sp_pack_rope_table(second, table, P, rope_type=rope_type, out_scale=c2)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(got_q), bits(want_q)), (rope_type, fp64_angles, middle, scaled, c2)
+            assert np.array_equal(bits(got_k), bits(want_k)), (rope_type, fp64_angles, middle, scaled, c2)
 
 
 @pytest.mark.parametrize("name,which", [("share_32768", "q"), ("tiny_231", "q"), ("cross_24576x1000", "k"),

@@ -56,10 +56,13 @@ hipError_t launch_rope_angles(const int32_t* pos, float* table_out, int64_t n_to
                               hipStream_t stream);
 
 // launch_rope_any's pack (ranks head shards) with the angles taken from such a
-// table, each (cos, sin) multiplied by out_scale.
-hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const float* table, int64_t n_tokens,
-                                  int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, bool split,
-                                  float out_scale, hipStream_t stream);
+// table, each (cos, sin) multiplied by out_scale.  With src2 (else null), a
+// second tensor of the same shape goes to dst2 in the same launch, its
+// (cos, sin) multiplied by out_scale2.
+hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
+                                  const float* table, int64_t n_tokens, int64_t batch, int32_t heads,
+                                  int32_t head_dim, int32_t ranks, bool split, float out_scale, float out_scale2,
+                                  hipStream_t stream);
 
 // Attention over [batch, nq, heads, head_dim] operands.  The output row of
 // (batch entry bb, token n, head h) is written at head slot

@@ -195,8 +195,22 @@ LTXA_EXPORT int ltxa_sp_pack_rope_table(const void* src, void* dst, const float*
                                              rope_type, out_scale);
   if (rc) return rc;
   return launch_status(ltxa::launch_rope_pack_table(
-      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), table, n_tokens, batch, heads, head_dim,
-      world_size, rope_type == LTXA_ROPE_SPLIT, out_scale != 0.0f ? out_scale : 1.0f,
+      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), nullptr, nullptr, table, n_tokens, batch,
+      heads, head_dim, world_size, rope_type == LTXA_ROPE_SPLIT, out_scale != 0.0f ? out_scale : 1.0f, 1.0f,
+      static_cast<hipStream_t>(stream)));
+}
+
+LTXA_EXPORT int ltxa_sp_pack_rope_qk_table(const void* q, void* q_dst, float q_scale, const void* k, void* k_dst,
+                                           float k_scale, const float* table, int64_t n_tokens, int64_t batch,
+                                           int32_t heads, int32_t head_dim, int32_t world_size, int32_t rope_type,
+                                           void* stream) {
+  const int rc = ltxa::check_pack_rope_qk_table(q, q_dst, q_scale, k, k_dst, k_scale, table, n_tokens, batch,
+                                                heads, head_dim, world_size, rope_type);
+  if (rc) return rc;
+  return launch_status(ltxa::launch_rope_pack_table(
+      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(q_dst), static_cast<const uint16_t*>(k),
+      static_cast<uint16_t*>(k_dst), table, n_tokens, batch, heads, head_dim, world_size,
+      rope_type == LTXA_ROPE_SPLIT, q_scale != 0.0f ? q_scale : 1.0f, k_scale != 0.0f ? k_scale : 1.0f,
       static_cast<hipStream_t>(stream)));
 }
 

@@ -30,6 +30,8 @@
 //    workgroup (one fp64 pow per pair, shared through LDS), and one thread
 //    owns one pair group of one token.  Lanes cover the groups of one head
 //    row, then tokens.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -270,22 +272,44 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
 // precompute_ltx_freqs_cis, applied later by apply_ltx_rotary_emb): entry
 // (n, i) = (cos, sin) of pair i of token n, from the same turn() as the
 // kernels above, unscaled, so a rotation read from the table equals the one
-// computed in place bit for bit.  One thread per (token, pair).
+// computed in place bit for bit.  One thread per pair and block of
+// kAngleTokens consecutive tokens: its schedule entry is read once and the
+// block's position loads are all in flight together (one thread per (token,
+// pair) waited for two dependent loads per entry: 9-10 us on a 32768-token,
+// 64-pair table, where writing it takes ~2 us).
+constexpr int kAngleTokens = 8;
 template <bool F64>
 __global__ __launch_bounds__(kThreads) void rope_angles_kernel(const int32_t* __restrict__ pos,
                                                                float2* __restrict__ out, int64_t n_tokens,
                                                                int32_t axes, int32_t half, int32_t log2_half,
                                                                double mid, RopeTable table) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= n_tokens * half) return;
   // A shift when half is a power of two (log2_half >= 0): 64-bit divides are
   // software loops.
-  const int64_t n = log2_half >= 0 ? t >> log2_half : t / half;
-  const int i = static_cast<int>(t - n * half);
+  const int64_t blk = log2_half >= 0 ? t >> log2_half : t / half;
+  const int i = static_cast<int>(t - blk * half);
+  const int64_t n0 = blk * kAngleTokens;
+  if (n0 >= n_tokens) return;
+  const int count = n_tokens - n0 < kAngleTokens ? static_cast<int>(n_tokens - n0) : kAngleTokens;
   const int a = table.axis[i];
-  float c = 1.0f, s = 0.0f;
-  if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[i], c, s);
-  out[t] = float2{c, s};
+  float c[kAngleTokens], s[kAngleTokens];
+  if (a >= 0) {
+    const double coef = table.coef[i];
+    int32_t p[kAngleTokens];
+#pragma unroll
+    for (int u = 0; u < kAngleTokens; ++u) p[u] = u < count ? pos[(n0 + u) * axes + a] : 0;
+#pragma unroll
+    for (int u = 0; u < kAngleTokens; ++u) turn<F64>(p[u], mid, coef, c[u], s[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kAngleTokens; ++u) {
+      c[u] = 1.0f;
+      s[u] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kAngleTokens; ++u)
+    if (u < count) out[(n0 + u) * half + i] = float2{c[u], s[u]};
 }
 
 // Pack + rotary with the angles read from that table.  Layout of the plain
@@ -301,15 +325,17 @@ __global__ __launch_bounds__(kThreads) void rope_angles_kernel(const int32_t* __
 // shared-grid kernel, which computes its sin/cos itself; building the table
 // takes ~10 us more, so the table pays where it serves several tensors or
 // layers, as the pages' precomputed frequencies do.
-template <bool SPLIT, int ROW, bool WHOLE>
+template <bool SPLIT, int ROW, bool WHOLE, bool TWO>
 __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* __restrict__ src,
                                                                    u32x4* __restrict__ dst,
+                                                                   const u32x4* __restrict__ src2,
+                                                                   u32x4* __restrict__ dst2,
                                                                    const float4* __restrict__ tab,
                                                                    int64_t n_tokens, int64_t batch,
                                                                    int32_t heads, int32_t head_dim,
                                                                    int32_t ranks, int32_t nblocks,
                                                                    int32_t log2_ranks, int32_t log2_groups,
-                                                                   float out_scale) {
+                                                                   float out_scale, float out_scale2) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
   // ROW > 0 fixes the 16-byte vectors per head row (head_dim / 8) at compile
   // time, so that the index arithmetic folds into shifts and constants;
@@ -317,10 +343,21 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
   const int row = ROW > 0 ? ROW : head_dim / 8;
   const int groups = SPLIT ? row / 2 : row;
   const int half = row * 4;
+  // TWO: a second tensor of the same shape (K beside Q) in the same launch,
+  // on workgroups of its own (the second half of each XCD's range).  Giving
+  // one thread the rows of both tensors was 4 % slower than two launches.
+  uint32_t lid = static_cast<uint32_t>(xcd_contiguous(blockIdx.x, TWO ? 2 * nblocks : nblocks));
+  if constexpr (TWO) {
+    if (lid >= static_cast<uint32_t>(nblocks)) {
+      lid -= nblocks;
+      src = src2;
+      dst = dst2;
+      out_scale = out_scale2;
+    }
+  }
   // Index arithmetic is a large part of a thread's work here: shifts when
   // the rank and group counts are powers of two (log2 >= 0), and no divide
   // by n_tokens for one batch entry.  (64-bit divides are software loops.)
-  const uint32_t lid = static_cast<uint32_t>(xcd_contiguous(blockIdx.x, nblocks));
   uint32_t p, blk;
   if (log2_ranks >= 0) {
     p = lid & ((1u << log2_ranks) - 1);
@@ -346,62 +383,69 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
     n = r - b * n_tokens;
   }
 
-  float c[PPT], s[PPT];
-  const float4* e = tab + (n * half + PPT * g) / 2;  // pairs PPT g .. PPT g + PPT - 1, two per float4
+  // Pairs PPT g .. PPT g + PPT - 1 of token n, two per float4.  They are
+  // scaled only after the first rows' loads are issued: scaling them first
+  // made every thread wait for its table entries before requesting any row.
+  const float4* e = tab + (n * half + PPT * g) / 2;
+  float4 tv[PPT / 2];
 #pragma unroll
-  for (int k = 0; k < PPT / 2; ++k) {
-    const float4 v = e[k];
-    c[2 * k] = v.x * out_scale;
-    s[2 * k] = v.y * out_scale;
-    c[2 * k + 1] = v.z * out_scale;
-    s[2 * k + 1] = v.w * out_scale;
-  }
+  for (int k = 0; k < PPT / 2; ++k) tv[k] = e[k];
+  float c[PPT], s[PPT];
+  auto scale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < PPT / 2; ++k) {
+      c[2 * k] = tv[k].x * out_scale;
+      s[2 * k] = tv[k].y * out_scale;
+      c[2 * k + 1] = tv[k].z * out_scale;
+      s[2 * k + 1] = tv[k].w * out_scale;
+    }
+  };
 
   // Vector g (and, split, g + row / 2) of this rank's head rows: the rows
   // are consecutive in both layouts, `row` vectors apart.
   const int32_t hl = heads / ranks;
   const u32x4* from = src + (r * heads + int64_t(p) * hl) * row + g;
   u32x4* to = dst + ((int64_t(p) * batch + b) * n_tokens + n) * hl * row + g;
-  auto rotate = [&](int j) __attribute__((always_inline)) {
+  // Rows j0 .. j0 + count - 1: every load issued before the first rotation
+  // (the compiler keeps that order: the pointers are restrict).
+  auto rows = [&](int32_t j0, auto count_c, auto first_c) __attribute__((always_inline)) {
+    constexpr int count = decltype(count_c)::value;
     if constexpr (SPLIT) {
-      u32x4 lo = __builtin_nontemporal_load(from + j * row);
-      u32x4 hi = __builtin_nontemporal_load(from + j * row + row / 2);
-      rotate_split(lo, hi, c, s);
-      __builtin_nontemporal_store(lo, to + j * row);
-      __builtin_nontemporal_store(hi, to + j * row + row / 2);
-    } else {
-      __builtin_nontemporal_store(rotate_interleaved(__builtin_nontemporal_load(from + j * row), c, s),
-                                  to + j * row);
-    }
-  };
-  // Whole groups of kRowsInFlight rows: all loads issued before the first
-  // rotation (the compiler keeps that order: the pointers are restrict).
-  int32_t j0 = 0;
-  for (; j0 + kRowsInFlight <= hl; j0 += kRowsInFlight) {
-    if constexpr (SPLIT) {
-      u32x4 lo[kRowsInFlight], hi[kRowsInFlight];
+      u32x4 lo[count], hi[count];
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
+      for (int u = 0; u < count; ++u) {
         lo[u] = __builtin_nontemporal_load(from + (j0 + u) * row);
         hi[u] = __builtin_nontemporal_load(from + (j0 + u) * row + row / 2);
       }
+      if constexpr (decltype(first_c)::value) scale();
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
+      for (int u = 0; u < count; ++u) {
         rotate_split(lo[u], hi[u], c, s);
         __builtin_nontemporal_store(lo[u], to + (j0 + u) * row);
         __builtin_nontemporal_store(hi[u], to + (j0 + u) * row + row / 2);
       }
     } else {
-      u32x4 w[kRowsInFlight];
+      u32x4 w[count];
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) w[u] = __builtin_nontemporal_load(from + (j0 + u) * row);
+      for (int u = 0; u < count; ++u) w[u] = __builtin_nontemporal_load(from + (j0 + u) * row);
+      if constexpr (decltype(first_c)::value) scale();
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u)
+      for (int u = 0; u < count; ++u)
         __builtin_nontemporal_store(rotate_interleaved(w[u], c, s), to + (j0 + u) * row);
     }
+  };
+  using group = std::integral_constant<int, kRowsInFlight>;
+  using one = std::integral_constant<int, 1>;
+  int32_t j0 = 0;
+  if (WHOLE || hl >= kRowsInFlight) {
+    rows(0, group{}, std::true_type{});
+    j0 = kRowsInFlight;
+  } else {
+    scale();
   }
+  for (; j0 + kRowsInFlight <= hl; j0 += kRowsInFlight) rows(j0, group{}, std::false_type{});
   if constexpr (!WHOLE)
-    for (; j0 < hl; ++j0) rotate(j0);
+    for (; j0 < hl; ++j0) rows(j0, one{}, std::false_type{});
 }
 
 template <bool SPLIT, bool F64>
@@ -466,7 +510,7 @@ hipError_t launch_rope_angles(const int32_t* pos, float* table_out, int64_t n_to
                               hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's error
   const int32_t half = head_dim / 2;
-  const int64_t blocks = (n_tokens * half + kThreads - 1) / kThreads;
+  const int64_t blocks = ((n_tokens + kAngleTokens - 1) / kAngleTokens * half + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   float2* out = reinterpret_cast<float2*>(table_out);
   const int32_t log2_half = (half & (half - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(half)) : -1;
@@ -479,9 +523,10 @@ hipError_t launch_rope_angles(const int32_t* pos, float* table_out, int64_t n_to
   return hipGetLastError();
 }
 
-hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const float* table, int64_t n_tokens,
-                                  int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks, bool split,
-                                  float out_scale, hipStream_t stream) {
+hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
+                                  const float* table, int64_t n_tokens, int64_t batch, int32_t heads,
+                                  int32_t head_dim, int32_t ranks, bool split, float out_scale, float out_scale2,
+                                  hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's error
   const int groups = head_dim / (split ? 16 : 8);
   const int64_t per_rank = (batch * n_tokens * groups + kThreads - 1) / kThreads;
@@ -492,27 +537,31 @@ hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const floa
   };
   const int32_t lr = log2_or_minus1(ranks), lg = log2_or_minus1(groups);
   const int64_t blocks = per_rank * ranks;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if ((src2 ? 2 * blocks : blocks) > 0x7fffffff) return hipErrorInvalidConfiguration;
   const float4* tab = reinterpret_cast<const float4*>(table);
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
-  const dim3 grid(static_cast<uint32_t>(blocks));
+  const u32x4* s2 = reinterpret_cast<const u32x4*>(src2);
+  u32x4* d2 = reinterpret_cast<u32x4*>(dst2);
+  // Two tensors: twice the workgroups.
+  const dim3 grid(static_cast<uint32_t>(src2 ? 2 * blocks : blocks));
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, s, d, tab, n_tokens, batch, heads, head_dim, ranks,
-                       static_cast<int32_t>(blocks), lr, lg, out_scale);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, s, d, s2, d2, tab, n_tokens, batch, heads,
+                       head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale, out_scale2);
   };
   // Specialised for the common shapes: head_dim 128 or 64 with whole groups
   // of kRowsInFlight heads per rank; every other shape takes the general form.
   const bool whole = (heads / ranks) % kRowsInFlight == 0;
-  if (split) {
-    if (whole && head_dim == 128) go(rope_pack_table_kernel<true, 16, true>);
-    else if (whole && head_dim == 64) go(rope_pack_table_kernel<true, 8, true>);
-    else go(rope_pack_table_kernel<true, 0, false>);
-  } else {
-    if (whole && head_dim == 128) go(rope_pack_table_kernel<false, 16, true>);
-    else if (whole && head_dim == 64) go(rope_pack_table_kernel<false, 8, true>);
-    else go(rope_pack_table_kernel<false, 0, false>);
-  }
+  auto pick = [&](auto split_c, auto two_c) {
+    constexpr bool S = decltype(split_c)::value, T = decltype(two_c)::value;
+    if (whole && head_dim == 128) go(rope_pack_table_kernel<S, 16, true, T>);
+    else if (whole && head_dim == 64) go(rope_pack_table_kernel<S, 8, true, T>);
+    else go(rope_pack_table_kernel<S, 0, false, T>);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (split) src2 ? pick(yes{}, yes{}) : pick(yes{}, no{});
+  else src2 ? pick(no{}, yes{}) : pick(no{}, no{});
   return hipGetLastError();
 }
 

@@ -245,6 +245,29 @@ inline int check_pack_rope_table(const void* src, const void* dst, const float* 
   return LTXA_OK;
 }
 
+// Q and K packed and rotated by one table in one launch: each pair as for
+// check_pack_rope_table, a grid of twice the workgroups, and neither
+// destination may overlap the other pair's tensors (the two sources may
+// overlap: they are only read).
+inline int check_pack_rope_qk_table(const void* q, const void* q_dst, float q_scale, const void* k,
+                                    const void* k_dst, float k_scale, const float* table, int64_t n_tokens,
+                                    int64_t batch, int32_t heads, int32_t head_dim, int32_t world_size,
+                                    int32_t rope_type) {
+  int rc = check_pack_rope_table(q, q_dst, table, n_tokens, batch, heads, head_dim, world_size, rope_type,
+                                 q_scale);
+  if (rc) return rc;
+  rc = check_pack_rope_table(k, k_dst, table, n_tokens, batch, heads, head_dim, world_size, rope_type, k_scale);
+  if (rc) return rc;
+  // One launch: twice the workgroups of one tensor, still below 2^31.
+  const int64_t groups = head_dim / (rope_type == LTXA_ROPE_SPLIT ? 16 : 8);
+  const int64_t threads = mul_capped(mul_capped(batch, n_tokens), groups);
+  if ((threads + 255) / 256 * world_size * 2 >= (INT64_C(1) << 31)) return LTXA_E_RANGE;
+  const int64_t bytes = mul4_capped(batch, n_tokens, heads, int64_t(head_dim) * 2);
+  if (overlap(q_dst, bytes, k, bytes) || overlap(q_dst, bytes, k_dst, bytes) || overlap(k_dst, bytes, q, bytes))
+    return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
 // One tensor rotated in place: x [batch, n_tokens, heads, head_dim] bf16.
 inline int check_rope_ex(const void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
                          const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, double theta,

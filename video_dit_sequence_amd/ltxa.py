@@ -37,7 +37,8 @@ LTXA_E_RANGE = -7
 EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack",
            "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
            "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_attn_fwd_log2q",
-           "ltxa_attn_fwd_unpack_log2q", "ltxa_rope_table", "ltxa_sp_pack_rope_table")
+           "ltxa_attn_fwd_unpack_log2q", "ltxa_rope_table", "ltxa_sp_pack_rope_table",
+           "ltxa_sp_pack_rope_qk_table")
 
 LTXA_ROPE_INTERLEAVED = 0
 LTXA_ROPE_SPLIT = 1
@@ -119,6 +120,9 @@ def lib() -> ctypes.CDLL:
         L.ltxa_rope_table.argtypes = [vp, i64, i32, dp, i32, ctypes.c_double, op, vp, vp]
         L.ltxa_sp_pack_rope_table.restype = ctypes.c_int
         L.ltxa_sp_pack_rope_table.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, vp]
+        L.ltxa_sp_pack_rope_qk_table.restype = ctypes.c_int
+        L.ltxa_sp_pack_rope_qk_table.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64,
+                                                 i32, i32, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -379,6 +383,43 @@ def sp_pack_rope_table(src: torch.Tensor, table: torch.Tensor, world_size: int, 
     return out
 
 
+def sp_pack_rope_qk_table(q: torch.Tensor, k: torch.Tensor, table: torch.Tensor, world_size: int,
+                          rope_type: str = "interleaved", q_scale: float = 0.0, k_scale: float = 0.0,
+                          q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None):
+    """Q and K, each bf16 ``[B, N, H, D]``, -> rotated ``[P, B, N, H/P, D]`` with
+    one :func:`rope_table`, in one launch (``ltxa_sp_pack_rope_qk_table``).
+
+    Returns ``(q_out, k_out)``, equal, bit for bit, to
+    :func:`sp_pack_rope_table` of each with its own scale.
+    """
+    _gpu(q, "q", torch.bfloat16)
+    _gpu(k, "k", torch.bfloat16)
+    _gpu(table, "table", torch.float32)
+    if q.shape != k.shape:
+        raise ValueError("q and k must have the same shape")
+    B, N, H, D = q.shape
+    P = int(world_size)
+    types = {"interleaved": LTXA_ROPE_INTERLEAVED, "split": LTXA_ROPE_SPLIT}
+    if rope_type not in types:
+        raise ValueError("rope_type must be 'interleaved' or 'split'")
+    if table.numel() != N * (D // 2) * 2:
+        raise ValueError("table must be [N, D/2, 2]")
+    outs = []
+    for o in (q_out, k_out):
+        if o is None:
+            if P < 1 or H % P:
+                _check("ltxa_sp_pack_rope_qk_table", LTXA_E_DIVISIBILITY if P >= 1 else LTXA_E_SHAPE)
+            o = torch.empty((P, B, N, H // P, D), dtype=q.dtype, device=q.device)
+        _gpu(o, "out", torch.bfloat16)
+        if o.numel() != q.numel():
+            raise ValueError("out has the wrong number of elements")
+        outs.append(o)
+    _check("ltxa_sp_pack_rope_qk_table", lib().ltxa_sp_pack_rope_qk_table(
+        q.data_ptr(), outs[0].data_ptr(), float(q_scale), k.data_ptr(), outs[1].data_ptr(), float(k_scale),
+        table.data_ptr(), N, B, H, D, P, types[rope_type], _stream_ptr(q)))
+    return outs[0], outs[1]
+
+
 def attn_fwd_unpack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nk_valid: Optional[int] = None,
                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, q_log2: bool = False) -> torch.Tensor:
@@ -507,11 +548,27 @@ class SpShare:
                 "o_shards": self._view("o_shards", (P, batch, N, Hl, D), device),
                 "out": self._view("out", (batch, N, self.num_heads, D), device)}
 
+    def rope_table_buffer(self, device) -> torch.Tensor:
+        """A view of the owned float32 ``[n_pad, head_dim/2, 2]`` buffer for
+        the step's angle table (:func:`rope_table`), sized on first use for
+        ``ceil(max_tokens / world_size) * world_size`` tokens."""
+        if self.n_pad < 1:
+            raise ValueError("call set_seqlen before asking for buffers")
+        half = max(self.head_dim // 2, 1)
+        numel = self.n_pad * half * 2
+        buf = self._store.get("rope_table")
+        if buf is None or buf.numel() < numel or buf.device != torch.device(device):
+            cap = self.tokens_per_rank_max * self.world_size * half * 2
+            buf = torch.empty(max(numel, cap), dtype=torch.float32, device=device)
+            self._store["rope_table"] = buf
+        return buf[:numel].view(self.n_pad, half, 2)
+
 
 def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpShare",
                  q_pos: torch.Tensor, q_max_pos, k_pos: Optional[torch.Tensor] = None,
                  k_max_pos=None, nk_valid: Optional[int] = None, theta: float = 10000.0,
-                 scale: Optional[float] = None, fused: bool = True, prescale_q: bool = True) -> torch.Tensor:
+                 scale: Optional[float] = None, fused: bool = True, prescale_q: bool = True,
+                 q_rope_table: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One layer's SP attention for every virtual rank of ``share`` on one GPU.
 
     ``q``: token-major bf16 ``[B, N_pad, H, D]`` padded to ``share.n_pad``
@@ -533,12 +590,23 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     given (``ltxa_attn_fwd_unpack_log2q``): Q is rounded once instead of
     twice.  With ``prescale_q=False`` the fused result is bit-identical to the
     unfused one.
+
+    Self-attention (``k_pos`` absent or the same tensor as ``q_pos``, the same
+    ``max_pos`` and token count) takes the fused path's table form, with the
+    same result bit for bit: the angles of ``q_pos`` go into a table
+    (``ltxa_rope_table``) and one launch exchanges and rotates Q and K with it
+    (``ltxa_sp_pack_rope_qk_table``).  ``q_rope_table`` is such a table made
+    by the caller (:func:`rope_table`, default options), once per forward
+    pass for every layer, as the pages precompute the rotary frequencies;
+    without it the table is built into the share's buffer on each call.
     """
     P = share.world_size
     B, N, H, D = q.shape
     Nk = k.shape[1]
     if N != share.n_pad or H != share.num_heads or D != share.head_dim:
         raise ValueError("q must be [B, share.n_pad, num_heads, head_dim]")
+    same_angles = ((k_pos is None or k_pos is q_pos) and Nk == N and
+                   (k_max_pos is None or [float(x) for x in k_max_pos] == [float(x) for x in q_max_pos]))
     k_pos = q_pos if k_pos is None else k_pos
     k_max_pos = q_max_pos if k_max_pos is None else k_max_pos
     nk_valid = share.n_valid if nk_valid is None else nk_valid
@@ -546,12 +614,15 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     buf = share.buffers(B, q.device, nk=Nk)
     qs, ks, vs, out = buf["q"], buf["k"], buf["v"], buf["out"]
     if fused:
-        if prescale_q:
-            c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale))
-            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs, out_scale=c)
+        c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale)) if prescale_q else 0.0
+        if same_angles:
+            table = q_rope_table
+            if table is None:
+                table = rope_table(q_pos, q_max_pos, D, theta, out=share.rope_table_buffer(q.device))
+            sp_pack_rope_qk_table(q, k, table, P, q_scale=c, q_out=qs, k_out=ks)
         else:
-            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs)
-        sp_pack_rope(k, k_pos, k_max_pos, P, theta, out=ks)
+            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs, out_scale=c if prescale_q else None)
+            sp_pack_rope(k, k_pos, k_max_pos, P, theta, out=ks)
         sp_pack(v, P, out=vs)
         attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale, out=out, q_log2=prescale_q)
     else:
