@@ -37,6 +37,7 @@ PACK_ROPE_CASES = [
     ("cross_24576x1000", 32, 8, "k"),  # audio keys, 1 axis, ragged 1000 of 1024
     ("share_32768", 32, 8, "q"),       # the timed configuration, D=128
     ("connector_1024", 32, 8, "k"),    # batch 2, 1-axis text positions, rows split over grid y
+    ("connector_1024", 32, 4, "q"),    # 8 heads per rank: two row groups per thread
 ]
 
 

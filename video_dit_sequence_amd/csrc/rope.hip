@@ -321,11 +321,11 @@ __global__ __launch_bounds__(kThreads) void rope_angles_kernel(const int32_t* __
 // consecutive logical workgroups on one XCD, which then reads each table row
 // into its L2 once (dealt round-robin, every XCD's L2 fetches the whole
 // table: +9 % in a timing probe).  Measured on MI355X on the [1, 32768, 32,
-// 128] -> 8 ranks tensor: 90.4-91.0 us, against 93.9-94.6 us for the
-// shared-grid kernel, which computes its sin/cos itself; building the table
-// takes ~10 us more, so the table pays where it serves several tensors or
-// layers, as the pages' precomputed frequencies do.
-template <bool SPLIT, int ROW, bool WHOLE, bool TWO>
+// 128] -> 8 ranks tensor: 89.1-90.5 us, against 93.7-94.1 us for the
+// shared-grid kernel, which computes its sin/cos itself; Q and K together in
+// one launch 177 us (6.07 TB/s), against ~190 us for two shared-grid
+// launches, and the table's build 6.8 us.
+template <bool SPLIT, int ROW, int HL, bool TWO>
 __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* __restrict__ src,
                                                                    u32x4* __restrict__ dst,
                                                                    const u32x4* __restrict__ src2,
@@ -337,9 +337,10 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
                                                                    int32_t log2_ranks, int32_t log2_groups,
                                                                    float out_scale, float out_scale2) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
-  // ROW > 0 fixes the 16-byte vectors per head row (head_dim / 8) at compile
-  // time, so that the index arithmetic folds into shifts and constants;
-  // WHOLE: heads / ranks is a multiple of kRowsInFlight (no partial group).
+  // ROW > 0 and HL > 0 fix the 16-byte vectors per head row (head_dim / 8)
+  // and the heads per rank (a multiple of kRowsInFlight) at compile time, so
+  // that the index arithmetic folds into shifts and constants.
+  static_assert(HL % kRowsInFlight == 0, "whole groups of rows");
   const int row = ROW > 0 ? ROW : head_dim / 8;
   const int groups = SPLIT ? row / 2 : row;
   const int half = row * 4;
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
 
   // Vector g (and, split, g + row / 2) of this rank's head rows: the rows
   // are consecutive in both layouts, `row` vectors apart.
-  const int32_t hl = heads / ranks;
+  const int32_t hl = HL > 0 ? HL : heads / ranks;
   const u32x4* from = src + (r * heads + int64_t(p) * hl) * row + g;
   u32x4* to = dst + ((int64_t(p) * batch + b) * n_tokens + n) * hl * row + g;
   // Rows j0 .. j0 + count - 1: every load issued before the first rotation
@@ -437,14 +438,14 @@ __global__ __launch_bounds__(kThreads) void rope_pack_table_kernel(const u32x4* 
   using group = std::integral_constant<int, kRowsInFlight>;
   using one = std::integral_constant<int, 1>;
   int32_t j0 = 0;
-  if (WHOLE || hl >= kRowsInFlight) {
+  if (HL > 0 || hl >= kRowsInFlight) {
     rows(0, group{}, std::true_type{});
     j0 = kRowsInFlight;
   } else {
     scale();
   }
   for (; j0 + kRowsInFlight <= hl; j0 += kRowsInFlight) rows(j0, group{}, std::false_type{});
-  if constexpr (!WHOLE)
+  if constexpr (HL == 0)
     for (; j0 < hl; ++j0) rows(j0, one{}, std::false_type{});
 }
 
@@ -549,14 +550,15 @@ hipError_t launch_rope_pack_table(const uint16_t* src, uint16_t* dst, const uint
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, s, d, s2, d2, tab, n_tokens, batch, heads,
                        head_dim, ranks, static_cast<int32_t>(blocks), lr, lg, out_scale, out_scale2);
   };
-  // Specialised for the common shapes: head_dim 128 or 64 with whole groups
-  // of kRowsInFlight heads per rank; every other shape takes the general form.
-  const bool whole = (heads / ranks) % kRowsInFlight == 0;
+  // Specialised for the common shape, 4 heads per rank of head_dim 128 or
+  // 64 (the index arithmetic of the general form costs ~1 % there); every
+  // other shape takes the general form.
+  const bool hl4 = heads / ranks == 4;
   auto pick = [&](auto split_c, auto two_c) {
     constexpr bool S = decltype(split_c)::value, T = decltype(two_c)::value;
-    if (whole && head_dim == 128) go(rope_pack_table_kernel<S, 16, true, T>);
-    else if (whole && head_dim == 64) go(rope_pack_table_kernel<S, 8, true, T>);
-    else go(rope_pack_table_kernel<S, 0, false, T>);
+    if (hl4 && head_dim == 128) go(rope_pack_table_kernel<S, 16, 4, T>);
+    else if (hl4 && head_dim == 64) go(rope_pack_table_kernel<S, 8, 4, T>);
+    else go(rope_pack_table_kernel<S, 0, 0, T>);
   };
   using yes = std::true_type;
   using no = std::false_type;
