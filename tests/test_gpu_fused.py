@@ -273,10 +273,14 @@ def test_self_attention_table_form_equals_per_tensor_form(prescale_q):
     a = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, prescale_q=prescale_q).clone()
     table = ltxa.rope_table(pg, w.q_max_pos, 128, w.theta)
     b = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, prescale_q=prescale_q, q_rope_table=table).clone()
-    c = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, k_pos=pg.clone(), prescale_q=prescale_q)
+    c = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, k_pos=pg.clone(), prescale_q=prescale_q).clone()
+    # A separate K position tensor with the caller's table: the table turns Q alone.
+    d = ltxa.sp_attention(q, k, v, share, pg, w.q_max_pos, k_pos=pg.clone(), prescale_q=prescale_q,
+                          q_rope_table=table)
     torch.cuda.synchronize()
     assert np.array_equal(bits(a), bits(c))
     assert np.array_equal(bits(b), bits(c))
+    assert np.array_equal(bits(d), bits(c))
 
 
 @pytest.mark.parametrize("name,heads,P,which", PACK_ROPE_CASES)

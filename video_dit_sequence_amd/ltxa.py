@@ -599,6 +599,7 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
     by the caller (:func:`rope_table`, default options), once per forward
     pass for every layer, as the pages precompute the rotary frequencies;
     without it the table is built into the share's buffer on each call.
+    For cross-attention such a table rotates Q alone.
     """
     P = share.world_size
     B, N, H, D = q.shape
@@ -621,7 +622,10 @@ def sp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, share: "SpSh
                 table = rope_table(q_pos, q_max_pos, D, theta, out=share.rope_table_buffer(q.device))
             sp_pack_rope_qk_table(q, k, table, P, q_scale=c, q_out=qs, k_out=ks)
         else:
-            sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs, out_scale=c if prescale_q else None)
+            if q_rope_table is not None:
+                sp_pack_rope_table(q, q_rope_table, P, out_scale=c, out=qs)
+            else:
+                sp_pack_rope(q, q_pos, q_max_pos, P, theta, out=qs, out_scale=c if prescale_q else None)
             sp_pack_rope(k, k_pos, k_max_pos, P, theta, out=ks)
         sp_pack(v, P, out=vs)
         attn_fwd_unpack(qs, ks, vs, nk_valid=nk_valid, scale=scale, out=out, q_log2=prescale_q)
