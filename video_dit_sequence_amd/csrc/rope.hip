@@ -30,6 +30,10 @@
 //    workgroup (one fp64 pow per pair, shared through LDS), and one thread
 //    owns one pair group of one token.  Lanes cover the groups of one head
 //    row, then tokens.
+// And a split of the shared grid into its two steps, as the page's
+// precomputed frequencies split it: an angle table (cos, sin per token and
+// pair) evaluated once, then a pack + rotation that reads it, for one tensor
+// or for Q and K in one launch (the self-attention path).
 #include <type_traits>
 
 #include "common.h"
