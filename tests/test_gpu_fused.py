@@ -257,6 +257,33 @@ TABLE_VARIANTS = [("interleaved", False, False, False), ("interleaved", False, F
                   ("interleaved", True, False, True), ("interleaved", False, True, False)]
 
 
+@pytest.mark.parametrize("B,N,H,D,P", [(2, 40, 6, 96, 2), (1, 48, 6, 96, 3), (1, 45, 9, 48, 3)])
+def test_table_pack_general_shapes(B, N, H, D, P):
+    # The general form of the table pack: pair groups per row that are not a
+    # power of two (head_dim 96 and 48), 3 ranks (no shift for the rank), 2 or
+    # 3 heads per rank (no whole group of 4), two batch entries.  One and two
+    # tensors per launch against the pack with angles computed in the pass.
+    print(f"table pack general B={B} N={N} H={H} D={D} P={P}", flush=True)
+    g = torch.Generator().manual_seed(N * H + D)
+    x = torch.randn(B, N, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    y = torch.randn(B, N, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    max_pos = (5.0, 7.0, 9.0)
+    pos = torch.stack([torch.randint(0, int(m), (N,), generator=g) for m in max_pos], 1).to(torch.int32).to(DEV)
+    for rope_type in ("interleaved", "split"):
+        if rope_type == "split" and D % 16:
+            continue
+        table = ltxa.rope_table(pos, max_pos, D, 10000.0)
+        for cq, ck in ((0.0, 0.0), (0.25, 0.0)):
+            got_x = ltxa.sp_pack_rope_table(x, table, P, rope_type=rope_type, out_scale=cq)
+            got_q, got_k = ltxa.sp_pack_rope_qk_table(x, y, table, P, rope_type=rope_type, q_scale=cq, k_scale=ck)
+            want_x = ltxa.sp_pack_rope(x, pos, max_pos, P, 10000.0, opts=ltxa.rope_opts(rope_type=rope_type, out_scale=cq))
+            want_y = ltxa.sp_pack_rope(y, pos, max_pos, P, 10000.0, opts=ltxa.rope_opts(rope_type=rope_type, out_scale=ck))
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(got_x), bits(want_x)), (rope_type, cq)
+            assert np.array_equal(bits(got_q), bits(want_x)), (rope_type, cq)
+            assert np.array_equal(bits(got_k), bits(want_y)), (rope_type, ck)
+
+
 @pytest.mark.parametrize("prescale_q", [True, False])
 def test_self_attention_table_form_equals_per_tensor_form(prescale_q):
     # sp_attention turns self-attention's Q and K with one angle table in one
