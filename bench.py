@@ -220,9 +220,10 @@ def secondary(ltxa, wl, dev, iters):
     o = torch.empty_like(q)
     opts = ltxa.rope_opts(grid_heads=w.heads)
 
+    assert list(w.q_max_pos) == list(w.k_max_pos)  # Q and K turn by the same angles
+
     def connector():
-        ltxa.rope(q, pos, w.q_max_pos, w.theta, opts=opts)
-        ltxa.rope(k, pos, w.k_max_pos, w.theta, opts=opts)
+        ltxa.rope_qk_ex(q, k, pos, w.q_max_pos, w.theta, opts=opts)
         ltxa.attn_fwd(q, k, v, nk_valid=w.nk_valid, out=o)
 
     def connector_attn_only():

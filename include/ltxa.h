@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define LTXA_VERSION 106 /* major*100 + minor */
+#define LTXA_VERSION 107 /* major*100 + minor */
 
 enum ltxa_status {
   LTXA_OK = 0,
@@ -262,6 +262,27 @@ typedef struct ltxa_rope_opts {
 int ltxa_rope_ex(void* x, const int32_t* pos, int64_t n_tokens, int32_t axes,
                  const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim,
                  double theta, const ltxa_rope_opts* opts, void* stream);
+
+/*
+ * ltxa_rope_qk_ex -- ltxa_rope_ex of Q and of K in one launch, for a layer
+ * whose queries and keys turn by the same positions and options (the text
+ * connector's self-attention on the FastVideo gemma page: one 1D position
+ * grid, laid over the inner dimension of all heads, applied to Q and K).
+ * Each angle is evaluated once for both tensors.
+ *   q, k: bf16 [batch, n_tokens, heads, head_dim], rotated in place; they
+ *     may not overlap.
+ *   opts: as for ltxa_rope_ex; its out_scale applies to q only.
+ *   k_scale: 0 (none), or finite and > 0: every rotated value of k is
+ *     multiplied by it before its one rounding.
+ * q and k equal, bit for bit, ltxa_rope_ex(q, ..., opts) and
+ * ltxa_rope_ex(k, ..., opts with out_scale = k_scale).
+ * Errors: those of ltxa_rope_ex for q; E_NULL (k NULL); E_SHAPE (k_scale
+ * neither 0 nor finite and > 0); E_ALIGN (k not 16-byte aligned); E_ALIAS
+ * (k overlaps q or pos).
+ */
+int ltxa_rope_qk_ex(void* q, void* k, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                    const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim,
+                    double theta, const ltxa_rope_opts* opts, float k_scale, void* stream);
 
 /*
  * ltxa_sp_pack_rope_ex -- ltxa_sp_pack_rope with the variants above: the

@@ -201,6 +201,20 @@ void rope_opts_checks() {
   };
   EXPECT(check_rope_ex(dev(kA), devpos(kC), 1024, 1, m, 2, 32, 128, 1e4, nullptr), LTXA_OK);
   EXPECT(check_rope_ex(nullptr, devpos(kC), 1024, 1, m, 2, 32, 128, 1e4, nullptr), LTXA_E_NULL);
+  // Q and K in one launch: k present, aligned, disjoint from q and the
+  // positions; k_scale 0 or finite and > 0.
+  auto qk = [&](uintptr_t k, float ks) {
+    return ltxa::check_rope_qk_ex(dev(kA), dev(k), devpos(kC), 1024, 1, m, 2, 32, 128, 1e4, nullptr, ks);
+  };
+  EXPECT(qk(kB, 0.0f), LTXA_OK);
+  EXPECT(qk(kB, 0.5f), LTXA_OK);
+  EXPECT(ltxa::check_rope_qk_ex(dev(kA), nullptr, devpos(kC), 1024, 1, m, 2, 32, 128, 1e4, nullptr, 0.0f),
+         LTXA_E_NULL);
+  EXPECT(qk(kB, -0.5f), LTXA_E_SHAPE);
+  EXPECT(qk(kB, std::numeric_limits<float>::infinity()), LTXA_E_SHAPE);
+  EXPECT(qk(kB + 8, 0.0f), LTXA_E_ALIGN);
+  EXPECT(qk(kA + 4096, 0.0f), LTXA_E_ALIAS);
+  EXPECT(qk(kC, 0.0f), LTXA_E_ALIAS);
   EXPECT(run(opts(0, 32, 0, 0, 0, 0)), LTXA_OK);
   EXPECT(run(opts(1, 32, 0, 1, 1, 0)), LTXA_OK);
   EXPECT(run(opts(2, 0, 0, 0, 0, 0)), LTXA_E_SHAPE);

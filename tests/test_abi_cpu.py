@@ -316,6 +316,21 @@ def test_pack_rope_qk_table_errors(L):
     assert f(A, B, 0.0, D_, C + 256, 0.0, C, *sizes, None) == ltxa.LTXA_E_ALIAS  # k_dst on the table
 
 
+def test_rope_qk_ex_errors(L):
+    f = L.ltxa_rope_qk_ex
+    mp = (ctypes.c_double * 3)(5.0, 7.0, 9.0)
+    # q, k, pos, n, axes, max_pos, batch, heads, head_dim, theta, opts, k_scale, stream
+    sizes = (232, 3, mp, 1, 4, 64, 10000.0, None)
+    assert f(A, None, C, *sizes, 0.0, None) == ltxa.LTXA_E_NULL
+    assert f(None, B, C, *sizes, 0.0, None) == ltxa.LTXA_E_NULL
+    assert f(A, B, C, *sizes, -1.0, None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B, C, *sizes, float("nan"), None) == ltxa.LTXA_E_SHAPE
+    assert f(A, B + 8, C, *sizes, 0.0, None) == ltxa.LTXA_E_ALIGN
+    assert f(A, A + 256, C, *sizes, 0.0, None) == ltxa.LTXA_E_ALIAS   # k overlaps q
+    assert f(A, C, C, *sizes, 0.0, None) == ltxa.LTXA_E_ALIAS         # k on the positions
+    assert f(A, B, C, 232, 3, mp, 1, 4, 63, 10000.0, None, 0.0, None) == ltxa.LTXA_E_SHAPE
+
+
 def test_sp_share_bookkeeping():
     s = ltxa.SpShare(max_tokens=32768, num_heads=32, head_dim=128, world_size=8)
     assert s.heads_per_rank == 4 and s.tokens_per_rank_max == 4096

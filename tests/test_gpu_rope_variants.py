@@ -81,6 +81,30 @@ def test_rope_variant_matches_oracle(name, heads, variant):
     assert exact > 0.995, exact
 
 
+@pytest.mark.parametrize("name,heads", [("tiny_231", 4), ("connector_1024", 32)])
+@pytest.mark.parametrize("variant", VARIANTS, ids=_name)
+def test_rope_qk_ex_equals_two_rope_ex(name, heads, variant):
+    # Q and K in one launch (each angle evaluated once for both) against one
+    # ltxa_rope_ex per tensor, with the same options: bit for bit, with and
+    # without scales of their own.
+    w = wl.WORKLOADS[name]
+    v = _opts(variant, heads)
+    print(f"rope_qk_ex {name} H={heads} {v}", flush=True)
+    q, k, _ = wl.qkv(w, heads=heads)
+    qpos, _ = wl.positions(w)
+    k = k[:, :q.shape[1]].contiguous()
+    pg = torch.from_numpy(qpos).to(DEV)
+    for cq, ck in ((0.0, 0.0), (ltxa.log2_domain_scale(w.scale), 0.0), (0.0, 0.75)):
+        a, b = q.to(DEV), k.to(DEV)
+        c, d = q.to(DEV), k.to(DEV)
+        ltxa.rope_qk_ex(a, b, pg, w.q_max_pos, w.theta, opts=ltxa.rope_opts(**v), q_scale=cq, k_scale=ck)
+        ltxa.rope(c, pg, w.q_max_pos, w.theta, opts=ltxa.rope_opts(**v), out_scale=cq)
+        ltxa.rope(d, pg, w.q_max_pos, w.theta, opts=ltxa.rope_opts(**v), out_scale=ck)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(a), bits(c)), (cq, ck)
+        assert np.array_equal(bits(b), bits(d)), (cq, ck)
+
+
 def test_default_options_are_rope_qk_bit_exact():
     w = wl.WORKLOADS["full_6144"]
     q, _, _ = wl.qkv(w)

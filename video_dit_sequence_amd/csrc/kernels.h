@@ -32,7 +32,8 @@ struct RopeMode {
   bool inner;   // RopeInner grid instead of the shared RopeTable
   bool f64;     // angles and sin/cos in fp64
   double mid;   // 0, or 0.5 for cell-middle positions
-  float out_scale = 1.0f;  // every output value is the rotated value times this
+  float out_scale = 1.0f;   // every output value is the rotated value times this
+  float out_scale2 = 1.0f;  // the same, for the second tensor of a two-tensor launch
 };
 
 hipError_t launch_perm(const void* src, void* dst, const PermPlan& plan, int world_size,
@@ -41,8 +42,8 @@ hipError_t launch_perm(const void* src, void* dst, const PermPlan& plan, int wor
 // Rotary embedding of src [batch, n_tokens, heads, head_dim] into dst
 // [ranks, batch, n_tokens, heads/ranks, head_dim]; ranks = 1 with dst = src
 // rotates in place.  A non-null src2 is a second tensor of the same shape
-// and positions, rotated into dst2 by the same launch, which computes the
-// angles once for both (shared grid only; the inner grid rejects it).
+// and positions, rotated into dst2 (scaled by mode.out_scale2) by the same
+// launch, which computes the angles once for both.
 hipError_t launch_rope_any(const uint16_t* src, uint16_t* dst, const uint16_t* src2, uint16_t* dst2,
                            const int32_t* pos, int64_t n_tokens, int32_t axes, int64_t batch, int32_t heads,
                            int32_t head_dim, int32_t ranks, const RopeMode& mode, const RopeTable& table,

@@ -61,8 +61,10 @@ ltxa::RopeMode rope_mode(const ltxa_rope_opts* opts) {
 
 int rope_launch(const void* src, void* dst, const int32_t* pos, int64_t n_tokens, int32_t axes,
                 const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, int32_t ranks,
-                double theta, const ltxa_rope_opts* opts, void* stream, void* second = nullptr) {
-  const ltxa::RopeMode mode = rope_mode(opts);
+                double theta, const ltxa_rope_opts* opts, void* stream, void* second = nullptr,
+                float second_scale = 0.0f) {
+  ltxa::RopeMode mode = rope_mode(opts);
+  if (second_scale != 0.0f) mode.out_scale2 = second_scale;
   return launch_status(ltxa::launch_rope_any(
       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(second),
       static_cast<uint16_t*>(second), pos, n_tokens, axes, batch, heads, head_dim, ranks, mode,
@@ -163,6 +165,16 @@ LTXA_EXPORT int ltxa_rope_ex(void* x, const int32_t* pos, int64_t n_tokens, int3
   const int rc = ltxa::check_rope_ex(x, pos, n_tokens, axes, max_pos, batch, heads, head_dim, theta, opts);
   if (rc) return rc;
   return rope_launch(x, x, pos, n_tokens, axes, max_pos, batch, heads, head_dim, 1, theta, opts, stream);
+}
+
+LTXA_EXPORT int ltxa_rope_qk_ex(void* q, void* k, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                                const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim,
+                                double theta, const ltxa_rope_opts* opts, float k_scale, void* stream) {
+  const int rc = ltxa::check_rope_qk_ex(q, k, pos, n_tokens, axes, max_pos, batch, heads, head_dim, theta, opts,
+                                        k_scale);
+  if (rc) return rc;
+  return rope_launch(q, q, pos, n_tokens, axes, max_pos, batch, heads, head_dim, 1, theta, opts, stream, k,
+                     k_scale);
 }
 
 LTXA_EXPORT int ltxa_sp_pack_rope_ex(const void* src, void* dst, const int32_t* pos, int64_t n_tokens,

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
                                                                int64_t n_tokens, int32_t axes, int64_t batch,
                                                                int32_t heads, int32_t head_dim, int32_t ranks,
                                                                int32_t rows_per, double mid, float out_scale,
-                                                               RopeTable table) {
+                                                               float out_scale2, RopeTable table) {
   constexpr int PPT = SPLIT ? 8 : 4;  // pairs per thread
   const int groups = head_dim / (2 * PPT);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -152,19 +152,21 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
   const int g = static_cast<int>(t - n * groups);
   if (n >= n_tokens) return;
 
-  float c[PPT], s[PPT];
+  float c[PPT], s[PPT], c2[PPT], s2[PPT];
 #pragma unroll
   for (int e = 0; e < PPT; ++e) {
     const int pair = PPT * g + e;
     const int a = table.axis[pair];
-    c[e] = 1.0f;
-    s[e] = 0.0f;
-    if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], c[e], s[e]);
+    float cr = 1.0f, sr = 0.0f;
+    if (a >= 0) turn<F64>(pos[n * axes + a], mid, table.coef[pair], cr, sr);
     // An output scale turns (cos, sin) into (k cos, k sin) once per token:
     // every row is then rotated and scaled with the same two fp32 operations
-    // per value and rounded to bf16 once.  k = 1 leaves both exact.
-    c[e] *= out_scale;
-    s[e] *= out_scale;
+    // per value and rounded to bf16 once.  k = 1 leaves both exact.  The
+    // second tensor has a scale of its own.
+    c[e] = cr * out_scale;
+    s[e] = sr * out_scale;
+    c2[e] = cr * out_scale2;
+    s2[e] = sr * out_scale2;
   }
 
   // This thread's chunk of the token's (batch, head) rows (grid y, rows_per
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
   const int64_t rows = batch * heads - first < rows_per ? batch * heads : first + rows_per;
   const int64_t row_stride = int64_t(heads) * head_dim;         // token stride of the source
   const int64_t rank_stride = batch * n_tokens * hl * head_dim;  // rank stride of the destination
-  auto all_rows = [&](const uint16_t* from, uint16_t* to) __attribute__((always_inline)) {
+  auto all_rows = [&](const uint16_t* from, uint16_t* to, const float* cs, const float* sn)
+                      __attribute__((always_inline)) {
     int64_t b = first / heads;
     int32_t h = static_cast<int32_t>(first - b * heads);
     int32_t j = h % hl;
@@ -204,19 +207,21 @@ __global__ __launch_bounds__(kThreads) void rope_shared_kernel(const uint16_t* s
         a[u] = cur;
         if (u < count) advance();
       }
-      rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
+      rotate_rows<SPLIT>(a, count, g, head_dim / 2, cs, sn);
     }
   };
-  all_rows(src, dst);
-  if (src2) all_rows(src2, dst2);
+  all_rows(src, dst, c, s);
+  if (src2) all_rows(src2, dst2, c2, s2);
 }
 
 template <bool SPLIT, bool F64>
 __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* src, uint16_t* dst,
+                                                              const uint16_t* src2, uint16_t* dst2,
                                                               const int32_t* __restrict__ pos,
                                                               int64_t n_tokens, int32_t axes, int64_t batch,
                                                               int32_t heads, int32_t head_dim, int32_t ranks,
-                                                              double mid, float out_scale, RopeInner grid) {
+                                                              double mid, float out_scale, float out_scale2,
+                                                              RopeInner grid) {
   constexpr int PPT = SPLIT ? 8 : 4;
   const int groups = head_dim / (2 * PPT);
   const int lanes_per_token = groups;
@@ -252,23 +257,31 @@ __global__ __launch_bounds__(kThreads) void rope_inner_kernel(const uint16_t* sr
   for (int i = 0; i < kInnerTokensPerThread; ++i) {
     const int64_t n = n0 + static_cast<int64_t>(i) * token_lanes;
     if (n >= n_tokens) break;
-    float c[PPT], s[PPT];
+    float c[PPT], s[PPT], c2[PPT], s2[PPT];
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
-      c[e] = 1.0f;
-      s[e] = 0.0f;
-      if (axis[e] >= 0) turn<F64>(pos[n * axes + axis[e]], mid, coef[e], c[e], s[e]);
-      c[e] *= out_scale;  // as in the shared-grid kernel
-      s[e] *= out_scale;
+      float cr = 1.0f, sr = 0.0f;
+      if (axis[e] >= 0) turn<F64>(pos[n * axes + axis[e]], mid, coef[e], cr, sr);
+      c[e] = cr * out_scale;  // as in the shared-grid kernel
+      s[e] = sr * out_scale;
+      c2[e] = cr * out_scale2;
+      s2[e] = sr * out_scale2;
     }
-    for (int64_t b0 = 0; b0 < batch; b0 += kRowsInFlight) {
-      RowAddr a[kRowsInFlight];
-      const int count = batch - b0 < kRowsInFlight ? static_cast<int>(batch - b0) : kRowsInFlight;
+    // The head's rows of every batch entry; then, if given, the same rows of
+    // the second tensor (K beside Q: the same angles, evaluated once).
+    auto all_rows = [&](const uint16_t* from, uint16_t* to, const float* cs, const float* sn)
+                        __attribute__((always_inline)) {
+      for (int64_t b0 = 0; b0 < batch; b0 += kRowsInFlight) {
+        RowAddr a[kRowsInFlight];
+        const int count = batch - b0 < kRowsInFlight ? static_cast<int>(batch - b0) : kRowsInFlight;
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u)
-        a[u] = row_addr(src, dst, b0 + u, n, h, n_tokens, heads, hl, batch, head_dim);
-      rotate_rows<SPLIT>(a, count, g, head_dim / 2, c, s);
-    }
+        for (int u = 0; u < kRowsInFlight; ++u)
+          a[u] = row_addr(from, to, b0 + u, n, h, n_tokens, heads, hl, batch, head_dim);
+        rotate_rows<SPLIT>(a, count, g, head_dim / 2, cs, sn);
+      }
+    };
+    all_rows(src, dst, c, s);
+    if (src2) all_rows(src2, dst2, c2, s2);
   }
 }
 
@@ -478,15 +491,14 @@ hipError_t launch_mode(const uint16_t* src, uint16_t* dst, const uint16_t* src2,
     hipLaunchKernelGGL((rope_shared_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks),
                        static_cast<uint32_t>(chunks)), dim3(kThreads), 0, stream, src, dst, src2, dst2, pos,
                        n_tokens, axes, batch, heads, head_dim, ranks, static_cast<int32_t>(rows_per), mode.mid,
-                       mode.out_scale, table);
+                       mode.out_scale, mode.out_scale2, table);
   } else {
-    if (src2) return hipErrorInvalidValue;
     const int64_t per_block = int64_t(kInnerTokensPerThread) * (kThreads / groups);
     const int64_t blocks = (n_tokens + per_block - 1) / per_block;
     if (blocks > 0x7fffffff || heads > 65535) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((rope_inner_kernel<SPLIT, F64>), dim3(static_cast<uint32_t>(blocks), heads),
-                       dim3(kThreads), 0, stream, src, dst, pos, n_tokens, axes, batch, heads, head_dim, ranks,
-                       mode.mid, mode.out_scale, inner);
+                       dim3(kThreads), 0, stream, src, dst, src2, dst2, pos, n_tokens, axes, batch, heads,
+                       head_dim, ranks, mode.mid, mode.out_scale, mode.out_scale2, inner);
   }
   return hipGetLastError();
 }

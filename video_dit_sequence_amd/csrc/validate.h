@@ -279,4 +279,20 @@ inline int check_rope_ex(const void* x, const int32_t* pos, int64_t n_tokens, in
   return check_rope_opts(opts, heads, head_dim, axes);
 }
 
+// Q and K rotated in place in one launch by the same positions and options:
+// q as for check_rope_ex, k non-null and disjoint from q, k_scale 0 (none)
+// or finite and > 0.
+inline int check_rope_qk_ex(const void* q, const void* k, const int32_t* pos, int64_t n_tokens, int32_t axes,
+                            const double* max_pos, int64_t batch, int32_t heads, int32_t head_dim, double theta,
+                            const ltxa_rope_opts* opts, float k_scale) {
+  if (!k) return LTXA_E_NULL;
+  const int rc = check_rope_ex(q, pos, n_tokens, axes, max_pos, batch, heads, head_dim, theta, opts);
+  if (rc) return rc;
+  if (k_scale != 0.0f && check_out_scale(k_scale) != LTXA_OK) return LTXA_E_SHAPE;
+  if (!aligned16(k)) return LTXA_E_ALIGN;
+  const int64_t bytes = mul4_capped(batch, n_tokens, heads, int64_t(head_dim) * 2);
+  if (overlap(q, bytes, k, bytes) || overlap(k, bytes, pos, mul_capped(n_tokens, axes) * 4)) return LTXA_E_ALIAS;
+  return LTXA_OK;
+}
+
 }  // namespace ltxa

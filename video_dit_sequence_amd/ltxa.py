@@ -38,7 +38,7 @@ EXPORTS = ("ltxa_version", "ltxa_status_string", "ltxa_sp_pack", "ltxa_sp_unpack
            "ltxa_rope_qk", "ltxa_attn_fwd", "ltxa_sp_pack_rope", "ltxa_attn_fwd_unpack",
            "ltxa_rope_ex", "ltxa_sp_pack_rope_ex", "ltxa_attn_fwd_log2q",
            "ltxa_attn_fwd_unpack_log2q", "ltxa_rope_table", "ltxa_sp_pack_rope_table",
-           "ltxa_sp_pack_rope_qk_table")
+           "ltxa_sp_pack_rope_qk_table", "ltxa_rope_qk_ex")
 
 LTXA_ROPE_INTERLEAVED = 0
 LTXA_ROPE_SPLIT = 1
@@ -120,6 +120,9 @@ def lib() -> ctypes.CDLL:
         L.ltxa_rope_table.argtypes = [vp, i64, i32, dp, i32, ctypes.c_double, op, vp, vp]
         L.ltxa_sp_pack_rope_table.restype = ctypes.c_int
         L.ltxa_sp_pack_rope_table.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, vp]
+        L.ltxa_rope_qk_ex.restype = ctypes.c_int
+        L.ltxa_rope_qk_ex.argtypes = [vp, vp, vp, i64, i32, ctypes.POINTER(ctypes.c_double), i64, i32, i32,
+                                      ctypes.c_double, vp, ctypes.c_float, vp]
         L.ltxa_sp_pack_rope_qk_table.restype = ctypes.c_int
         L.ltxa_sp_pack_rope_qk_table.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64,
                                                  i32, i32, i32, i32, vp]
@@ -274,6 +277,26 @@ def rope(x: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
     _check("ltxa_rope_ex", lib().ltxa_rope_ex(
         x.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos), B, H, D, float(theta),
         None if opts is None else ctypes.byref(opts), _stream_ptr(x)))
+
+
+def rope_qk_ex(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, max_pos, theta: float = 10000.0,
+               opts: Optional[RopeOpts] = None, q_scale: Optional[float] = None, k_scale: float = 0.0) -> None:
+    """Rotate bf16 ``q`` and ``k`` (both ``[B, N, H, D]``) in place by the same
+    positions and options in one launch (``ltxa_rope_qk_ex``): equal, bit for
+    bit, to :func:`rope` of each.  ``q_scale`` overrides ``opts.out_scale``
+    for ``q``; ``k_scale`` (0: none) scales ``k``."""
+    opts = _with_scale(opts, q_scale)
+    _gpu(q, "q", torch.bfloat16)
+    _gpu(k, "k", torch.bfloat16)
+    _gpu(pos, "pos", torch.int32)
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must be [B, N, H, D] of one shape")
+    B, N, H, D = q.shape
+    if pos.dim() != 2 or pos.shape[0] != N or pos.shape[1] != len(max_pos):
+        raise ValueError("pos must be [N, A] with one max_pos per axis")
+    _check("ltxa_rope_qk_ex", lib().ltxa_rope_qk_ex(
+        q.data_ptr(), k.data_ptr(), pos.data_ptr(), N, pos.shape[1], _max_pos_array(max_pos), B, H, D,
+        float(theta), None if opts is None else ctypes.byref(opts), float(k_scale), _stream_ptr(q)))
 
 
 def _with_scale(opts: Optional[RopeOpts], out_scale: Optional[float]) -> Optional[RopeOpts]:
@@ -662,10 +685,7 @@ def connector_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: 
     """
     H, D = q.shape[2], q.shape[3]
     opts = rope_opts(rope_type=rope_type, grid_heads=H, fp64_angles=fp64_angles)
-    if prescale_q:
-        c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale))
-        rope(q, pos, max_pos, theta, opts=opts, out_scale=c)
-    else:
-        rope(q, pos, max_pos, theta, opts=opts)
-    rope(k, pos, max_pos, theta, opts=opts)
+    c = log2_domain_scale((1.0 / D ** 0.5) if scale is None else float(scale)) if prescale_q else 0.0
+    # Q and K share the positions: one launch evaluates each angle once for both.
+    rope_qk_ex(q, k, pos, max_pos, theta, opts=opts, q_scale=c)
     return attn_fwd(q, k, v, nk_valid=nk_valid, scale=scale, q_log2=prescale_q)
