@@ -30,8 +30,14 @@ def _path(q, k, v, qpos, kpos, q_max, k_max, n_valid, nk_valid, P, heads, D, sel
     q, qpos = q[:, :n_pad].contiguous(), qpos[:n_pad]
     if self_attn:
         k, v, kpos = k[:, :n_pad].contiguous(), v[:, :n_pad].contiguous(), kpos[:n_pad]
-    o = ltxa.sp_attention(q.to(DEV), k.to(DEV), v.to(DEV), share, torch.from_numpy(qpos).to(DEV), q_max,
-                          torch.from_numpy(kpos).to(DEV), k_max, nk_valid=nk_valid)
+        # Self-attention as the bench calls it: no K positions of their own,
+        # so Q and K turn by one angle table in one launch.
+        assert np.array_equal(qpos, kpos) and list(q_max) == list(k_max)
+        o = ltxa.sp_attention(q.to(DEV), k.to(DEV), v.to(DEV), share, torch.from_numpy(qpos).to(DEV), q_max,
+                              nk_valid=nk_valid)
+    else:
+        o = ltxa.sp_attention(q.to(DEV), k.to(DEV), v.to(DEV), share, torch.from_numpy(qpos).to(DEV), q_max,
+                              torch.from_numpy(kpos).to(DEV), k_max, nk_valid=nk_valid)
     torch.cuda.synchronize()
     return o
 
